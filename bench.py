@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Benchmark of one MLA decode step (absorbed-MQA form) on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic inputs:
+the split-KV attention kernel over the paged latent cache followed by the LSE
+combine (mla_decode_fwd_split + mla_decode_fwd_combine on one stream, which is
+what mla_decode_fwd launches).  The split plan is made once per step for all
+layers of a model, so it is timed separately and reported as ``plan_us``.
+
+Default workload: batch 16, s_q 1, 16 heads, 65536-token contexts over a
+shuffled pool of 64-token bf16 pages (about 1.2 GB of cache), values N(0,1).
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+
+
+def log(msg: str) -> None:
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for f in ("mla_decode_kernels.h", "mla_decode.hip"):
+        with open(os.path.join(ROOT, "mla_decode_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per split-kernel launch from committed rocprofv3 PMC runs, if they match this source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_split_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(case, o_gpu, lse_gpu, n_seqs: int, threads: int):
+    """Time the fp64 oracle on the host cores for the first n_seqs sequences (all their rows)."""
+    import numpy as np
+
+    import oracle
+    from mla_decode_attention_amd import workloads as W
+
+    n_seqs = max(1, min(n_seqs, case.batch))
+    rows = np.arange(n_seqs * case.s_q * case.heads, dtype=np.int64)
+    oracle.default()   # load (and if needed build) outside the timed region
+    t0 = time.perf_counter()
+    ro, rl = oracle.mla_decode(case.q, case.cache, case.block_table, case.seqlens, case.softmax_scale, case.causal,
+                               rows=rows, threads=threads)
+    dt = time.perf_counter() - t0
+    sample_bytes = W.algorithmic_bytes(case.seqlens[:n_seqs], n_seqs, case.s_q, case.heads)
+    err = np.abs(o_gpu.reshape(case.rows, -1)[rows] - ro)
+    rl_ok = np.isfinite(rl)
+    parity = dict(rows=int(rows.size), o_maxabs=float(err.max()), o_rmse=float(np.sqrt(np.mean(err ** 2))),
+                  lse_rel=float(np.max(np.abs(lse_gpu.reshape(-1)[rows][rl_ok] - rl[rl_ok])
+                                       / np.maximum(1.0, np.abs(rl[rl_ok])))))
+    return dict(value=sample_bytes / dt / 1e12, unit="TB/s", cores=threads, kind="oracle",
+                sample=f"{n_seqs} of {case.batch} sequences, all {case.s_q * case.heads} query rows each "
+                       f"({rows.size} rows, {sample_bytes / 1e6:.1f} MB algorithmic), fp64 C oracle",
+                seconds=dt), parity
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None, help="workload name (default: the headline long-context one)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-seqs", type=int, default=16)
+    ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (default: min(16, usable cores))")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (for scaling PMC byte counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE={world}); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import mla_decode_attention_amd as mla
+    from mla_decode_attention_amd import workloads as W
+    from mla_decode_attention_amd.inputs import bf16_bits_to_f32
+
+    name = args.workload or W.HEADLINE
+    if not os.path.exists(mla.LIB_PATH):
+        from mla_decode_attention_amd import build as hip_build
+        hip_build.build()
+    mla.lib()
+    dev = torch.device("cuda:0")
+    log(f"workload {name}: generating inputs")
+    case = W.build(name)
+    q = torch.from_numpy(case.q.view(np.int16)).to(dev).view(torch.bfloat16)
+    cache = torch.from_numpy(case.cache.view(np.int16)).to(dev).view(torch.bfloat16)
+    bt = torch.from_numpy(case.block_table).to(dev)
+    sl = torch.from_numpy(case.seqlens).to(dev)
+    b, s_q, h = case.batch, case.s_q, case.heads
+    ws = torch.empty(mla.workspace_size(b, s_q, h), dtype=torch.uint8, device=dev)
+    out = torch.empty((b, s_q, h, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((b, s_q, h), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    log(f"inputs on device: cache {cache.numel() * 2 / 1e9:.3f} GB, workspace {ws.numel() / 1e6:.1f} MB")
+
+    # plan (once per decode step for every layer): timed on its own
+    torch.cuda.synchronize()
+    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    mla.plan(sl, s_q, h, ws)
+    p0.record(stream)
+    for _ in range(10):
+        mla.plan(sl, s_q, h, ws)
+    p1.record(stream)
+    torch.cuda.synchronize()
+    plan_us = p0.elapsed_time(p1) * 1e3 / 10
+
+    def step():
+        mla.fwd_split(q, cache, bt, sl, case.softmax_scale, case.causal, ws)
+        mla.fwd_combine(sl, bt.shape[1], s_q, h, ws, out, lse)
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"timing {K} steps")
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for k in range(K):
+        ev_a[k].record(stream)
+        mla.fwd_split(q, cache, bt, sl, case.softmax_scale, case.causal, ws)
+        ev_b[k].record(stream)
+        mla.fwd_combine(sl, bt.shape[1], s_q, h, ws, out, lse)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / K
+    split_ms = [ev_a[k].elapsed_time(ev_b[k]) for k in range(K)]
+    split_avg_ms = float(np.mean(split_ms))
+    log(f"step {ms_per_step * 1e3:.1f} us (split kernel {split_avg_ms * 1e3:.1f} us avg, "
+        f"median {np.median(split_ms) * 1e3:.1f} us), plan {plan_us:.1f} us")
+
+    step_bytes = W.algorithmic_bytes(case.seqlens, b, s_q, h)
+    step_flops = W.algorithmic_flops(case.seqlens, s_q, h, case.causal)
+    kv_q_bytes = int(case.seqlens.astype(np.int64).sum()) * W.ROW_BYTES + b * s_q * h * 576 * 2
+    tbs = step_bytes / (ms_per_step * 1e-3) / 1e12
+    split_gbs = kv_q_bytes / (split_avg_ms * 1e-3) / 1e9
+    mfma_util = step_flops / (ms_per_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS
+
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy of {args.calib_copy_mib} MiB done")
+        del src, dst
+
+    o_gpu = bf16_bits_to_f32(out.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+    lse_gpu = lse.cpu().numpy().astype(np.float64)
+
+    cpu, parity = None, None
+    if not args.no_cpu_baseline:
+        try:
+            usable = len(os.sched_getaffinity(0))
+        except AttributeError:
+            usable = os.cpu_count() or 1
+        threads = args.cpu_threads or min(16, usable)
+        log(f"cpu baseline: fp64 oracle on {threads} threads, {args.cpu_sample_seqs} sequences")
+        cpu, parity = cpu_baseline(case, o_gpu, lse_gpu, args.cpu_sample_seqs, threads)
+        log(f"cpu baseline {cpu['seconds']:.1f} s -> {cpu['value']:.3e} TB/s; parity {parity}")
+
+    line = {
+        "metric": "MLA decode achieved HBM TB/s (% of peak) + us/step, b16 h16 64K ctx",
+        "value": round(tbs, 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "pct_of_hbm_peak": round(100 * tbs * 1e3 / HBM_PEAK_GBS, 2),
+        "mfma_util": round(mfma_util, 4),
+        "plan_us": round(plan_us, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 latent cache and queries; no model weights)",
+        "config": {"workload": name, "batch": b, "s_q": s_q, "heads": h,
+                   "context": int(case.seqlens.max()), "page_size": 64, "d_k": 576, "d_v": 512,
+                   "causal": bool(case.causal), "algorithmic_bytes": step_bytes, "algorithmic_flops": step_flops},
+        "roofline": {"bound": "hbm", "kernel": "split_kernel", "achieved": round(split_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(split_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(name), "avg_launch_us": round(split_avg_ms * 1e3, 2),
+                     "algorithmic_bytes_per_launch": kv_q_bytes},
+        "cpu_baseline": cpu,
+        "parity_vs_oracle": parity,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,139 @@
+/*
+ * mla_decode.h -- C ABI of the MI355X (gfx950) MLA decode attention library.
+ *
+ * The operation is decode-time attention of Multi-Head Latent Attention in its
+ * absorbed-MQA form (GQLA summary, section "Arquitetura": every query head
+ * attends the shared compressed latent cache directly; a cache row is the
+ * latent plus one shared RoPE key).  For every sequence b, query token
+ * i < s_q and head h, with n visible keys k_0..k_{n-1} (rows of the paged cache):
+ *
+ *     s_j = softmax_scale * dot(q[b,i,h,0:576], k_j[0:576])
+ *     LSE = ln sum_j exp(s_j)
+ *     O   = sum_j exp(s_j - LSE) * k_j[0:512]        (the value is the first 512 dims)
+ *
+ * i.e. standard attention S = Q K^T, P = softmax(S), O = P V (FlashMLA-ETAP
+ * summary, section "Mecanismo Central"), which the kernels evaluate in the
+ * transposed order S^T = K Q^T, O^T = V^T P^T the same section describes.
+ * Query length is 1-2 tokens and contexts reach 64K tokens (same summary,
+ * "Declaracao do Problema"); 16 heads is one GPU's share of 128.
+ *
+ * Visible keys: n = L_b when causal == 0; when causal != 0 token i sees keys
+ * 0 .. L_b - s_q + i (the s_q new tokens are the last s_q cache rows).  A row
+ * with no visible key yields O = 0 and LSE = -inf.
+ *
+ * Conventions shared by every entry point:
+ *   - All data pointers are DEVICE pointers owned by the caller.  The library
+ *     never frees them and allocates no device memory of its own.
+ *   - Every call is asynchronous and stream-ordered on `stream` (a hipStream_t,
+ *     NULL = the null stream); none synchronises the host.
+ *   - The current HIP device is the one used; pointers must live on it.
+ *   - Arguments are validated before any HIP call; errors are returned as
+ *     negative mla_status codes, never as aborts or exceptions.
+ *   - Results are deterministic for a given plan (same inputs, same bits).
+ */
+#ifndef MLA_DECODE_H_
+#define MLA_DECODE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Cache geometry fixed by the absorbed MLA layout. */
+#define MLA_DECODE_D_K 576      /* latent (512) + shared RoPE key (64) */
+#define MLA_DECODE_D_V 512      /* value = first 512 dims of a cache row */
+#define MLA_DECODE_PAGE_SIZE 64 /* tokens per cache page */
+
+typedef enum mla_status {
+    MLA_OK = 0,
+    MLA_ERR_INVALID_ARG = -1,         /* null pointer, non-positive size, non-finite scale ... */
+    MLA_ERR_UNSUPPORTED = -2,         /* valid but unsupported: heads, s_q or page size */
+    MLA_ERR_WORKSPACE_TOO_SMALL = -3, /* workspace_bytes below mla_decode_workspace_size() */
+    MLA_ERR_NO_DEVICE = -4,           /* no usable gfx950 HIP device */
+    MLA_ERR_HIP = -5                  /* a HIP runtime call failed (launch, attribute query) */
+} mla_status;
+
+/*
+ * Bytes of device workspace that mla_decode_plan / mla_decode_fwd need for this
+ * shape on the current device (the split count scales with its compute units).
+ *   batch      >= 1 sequences
+ *   s_q        1 or 2 query tokens per sequence
+ *   num_heads  16, 32, 64 or 128
+ *   bytes      out: required size
+ * Returns MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED or MLA_ERR_NO_DEVICE.
+ */
+int mla_decode_workspace_size(int batch, int s_q, int num_heads, size_t *bytes);
+
+/*
+ * Split-KV plan: reads seqlens on the device and writes into `workspace` a
+ * balanced partition of all sequences' cache pages into work items sized for
+ * the device's compute units (a long sequence is cut into several items whose
+ * partial results mla_decode_fwd merges by LSE).  One plan serves every layer
+ * of a decode step as long as seqlens, batch, s_q and num_heads are unchanged.
+ *   seqlens    int32 [batch], device: context length L_b >= 0 of each sequence,
+ *              counting the s_q new tokens
+ *   workspace  device buffer of at least mla_decode_workspace_size() bytes; its
+ *              contents are owned by the library until the fwd calls using it
+ *              have completed on `stream`
+ * Returns MLA_OK or an error code (nothing is launched on error).
+ */
+int mla_decode_plan(const int32_t *seqlens, int batch, int s_q, int num_heads, void *workspace,
+                    size_t workspace_bytes, void *stream);
+
+/*
+ * Decode attention for one layer, using a plan made by mla_decode_plan with the
+ * same seqlens, batch, s_q and num_heads.
+ *   q            bf16 [batch][s_q][num_heads][576], contiguous
+ *   kv_cache     bf16 [num_pages][64][576], contiguous paged latent cache
+ *   block_table  int32 [batch][bt_stride]: entry p of row b is the pool page
+ *                holding tokens 64p .. 64p+63 of sequence b; entries at or past
+ *                ceil(L_b / 64) are never read
+ *   bt_stride    int32 entries per block_table row (>= 1)
+ *   seqlens      int32 [batch], the same values the plan was made from
+ *   num_pages    pages in kv_cache (>= 1); page_size must be 64
+ *   softmax_scale  finite scale applied to q.k (e.g. 1/sqrt(192))
+ *   causal       0: every query token sees all L_b keys; 1: bottom-right causal
+ *   out          bf16 [batch][s_q][num_heads][512], written (round to nearest even)
+ *   lse          fp32 [batch][s_q][num_heads], natural-log LSE, written
+ * Device-side input errors do not fault: a sequence whose L_b is negative or
+ * exceeds 64*bt_stride, or whose block_table names a page outside
+ * [0, num_pages), or a plan made for other seqlens/shape, gets NaN in every
+ * out/lse element of that sequence (the whole batch for a shape mismatch).
+ * Cache rows past L_b in a sequence's last page are never read.
+ * Returns MLA_OK or an error code (nothing is launched on error).
+ */
+int mla_decode_fwd(const void *q, const void *kv_cache, const int32_t *block_table, int bt_stride,
+                   const int32_t *seqlens, int batch, int s_q, int num_heads, int num_pages,
+                   int page_size, float softmax_scale, int causal, void *workspace,
+                   size_t workspace_bytes, void *out, float *lse, void *stream);
+
+/*
+ * The two halves of mla_decode_fwd, for callers that merge partial results
+ * themselves or time the halves apart.  mla_decode_fwd_split runs the split-KV
+ * attention over the plan's work items and leaves each item's normalised
+ * partial output (fp32) and LSE in `workspace`; mla_decode_fwd_combine merges
+ * them per (sequence, query token, head) by LSE -- with M = max_s LSE_s,
+ * LSE = M + ln sum_s exp(LSE_s - M) and O = sum_s exp(LSE_s - LSE) O_s -- and
+ * writes `out` and `lse` exactly as mla_decode_fwd does.  Calling split then
+ * combine on one stream is bit-identical to mla_decode_fwd.  Arguments mean
+ * what they mean for mla_decode_fwd; the combine needs no cache inputs.
+ */
+int mla_decode_fwd_split(const void *q, const void *kv_cache, const int32_t *block_table,
+                         int bt_stride, const int32_t *seqlens, int batch, int s_q, int num_heads,
+                         int num_pages, int page_size, float softmax_scale, int causal,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+int mla_decode_fwd_combine(const int32_t *seqlens, int bt_stride, int batch, int s_q,
+                           int num_heads, void *workspace, size_t workspace_bytes, void *out,
+                           float *lse, void *stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *mla_decode_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H_ */

@@ -1,0 +1,191 @@
+"""MLA decode attention (absorbed-MQA form) for AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding over the C ABI of ``libmla_decode.so`` (declared in
+``include/mla_decode.h``).  The functions here only marshal arguments: they
+check dtypes, shapes and devices of torch tensors, pass raw device pointers and
+the current HIP stream, and turn negative status codes into exceptions.  Every
+step of the computation runs in the library's HIP kernels; there is no CPU or
+PyTorch fallback -- if the library is missing, :func:`lib` raises.
+
+Names follow the C ABI:
+  * :func:`workspace_size` -> ``mla_decode_workspace_size``
+  * :func:`plan`           -> ``mla_decode_plan``
+  * :func:`fwd`            -> ``mla_decode_fwd``
+  * :func:`fwd_split`      -> ``mla_decode_fwd_split``   (first half of fwd)
+  * :func:`fwd_combine`    -> ``mla_decode_fwd_combine`` (second half of fwd)
+  * :func:`status_string`  -> ``mla_decode_status_string``
+plus :func:`decode`, which allocates the workspace/outputs and calls plan + fwd.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+D_K = 576
+D_V = 512
+PAGE_SIZE = 64
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmla_decode.so")
+_LIB: ctypes.CDLL | None = None
+
+STATUS = {0: "MLA_OK", -1: "MLA_ERR_INVALID_ARG", -2: "MLA_ERR_UNSUPPORTED",
+          -3: "MLA_ERR_WORKSPACE_TOO_SMALL", -4: "MLA_ERR_NO_DEVICE", -5: "MLA_ERR_HIP"}
+EXPORTS = ("mla_decode_workspace_size", "mla_decode_plan", "mla_decode_fwd", "mla_decode_fwd_split",
+           "mla_decode_fwd_combine", "mla_decode_status_string")
+
+
+class MlaDecodeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {status_string(status)} ({status})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (built in-tree); raises if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run `python -m mla_decode_attention_amd.build` "
+                          "(or __graft_entry__.build()) first")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    L.mla_decode_workspace_size.argtypes = [I, I, I, ctypes.POINTER(SZ)]
+    L.mla_decode_workspace_size.restype = I
+    L.mla_decode_plan.argtypes = [P, I, I, I, P, SZ, P]
+    L.mla_decode_plan.restype = I
+    L.mla_decode_fwd.argtypes = [P, P, P, I, P, I, I, I, I, I, ctypes.c_float, I, P, SZ, P, P, P]
+    L.mla_decode_fwd.restype = I
+    L.mla_decode_fwd_split.argtypes = [P, P, P, I, P, I, I, I, I, I, ctypes.c_float, I, P, SZ, P]
+    L.mla_decode_fwd_split.restype = I
+    L.mla_decode_fwd_combine.argtypes = [P, I, I, I, I, P, SZ, P, P, P]
+    L.mla_decode_fwd_combine.restype = I
+    L.mla_decode_status_string.argtypes = [I]
+    L.mla_decode_status_string.restype = ctypes.c_char_p
+    _LIB = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().mla_decode_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise MlaDecodeError(fn, status)
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def workspace_size(batch: int, s_q: int, num_heads: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check("mla_decode_workspace_size", lib().mla_decode_workspace_size(int(batch), int(s_q), int(num_heads),
+                                                                         ctypes.byref(out)))
+    return int(out.value)
+
+
+def _require(t, name, dtype, ndim=None, device=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def plan(seqlens, s_q: int, num_heads: int, workspace, stream=None) -> None:
+    """mla_decode_plan: split metadata for these seqlens into ``workspace`` (uint8 device tensor)."""
+    import torch
+    _require(seqlens, "seqlens", torch.int32, 1)
+    _require(workspace, "workspace", torch.uint8, 1, seqlens.device)
+    _check("mla_decode_plan", lib().mla_decode_plan(seqlens.data_ptr(), seqlens.shape[0], int(s_q), int(num_heads),
+                                                    workspace.data_ptr(), workspace.numel(), _stream(stream)))
+
+
+def fwd(q, kv_cache, block_table, seqlens, softmax_scale: float, causal: bool, workspace, out, lse,
+        stream=None) -> None:
+    """mla_decode_fwd: O bf16 [b, s_q, h, 512] into ``out`` and LSE fp32 [b, s_q, h] into ``lse``."""
+    import torch
+    _require(q, "q", torch.bfloat16, 4)
+    dev = q.device
+    _require(kv_cache, "kv_cache", torch.bfloat16, 3, dev)
+    _require(block_table, "block_table", torch.int32, 2, dev)
+    _require(seqlens, "seqlens", torch.int32, 1, dev)
+    _require(workspace, "workspace", torch.uint8, 1, dev)
+    _require(out, "out", torch.bfloat16, 4, dev)
+    _require(lse, "lse", torch.float32, 3, dev)
+    b, s_q, h, dk = q.shape
+    if dk != D_K or kv_cache.shape[2] != D_K:
+        raise ValueError("q and kv_cache rows must be 576 wide")
+    if tuple(out.shape) != (b, s_q, h, D_V) or tuple(lse.shape) != (b, s_q, h):
+        raise ValueError("out must be [b, s_q, h, 512] and lse [b, s_q, h]")
+    if block_table.shape[0] != b or seqlens.shape[0] != b:
+        raise ValueError("block_table and seqlens need one row per sequence")
+    _check("mla_decode_fwd", lib().mla_decode_fwd(
+        q.data_ptr(), kv_cache.data_ptr(), block_table.data_ptr(), block_table.shape[1], seqlens.data_ptr(),
+        b, s_q, h, kv_cache.shape[0], kv_cache.shape[1], float(softmax_scale), int(bool(causal)),
+        workspace.data_ptr(), workspace.numel(), out.data_ptr(), lse.data_ptr(), _stream(stream)))
+
+
+def fwd_split(q, kv_cache, block_table, seqlens, softmax_scale: float, causal: bool, workspace,
+              stream=None) -> None:
+    """mla_decode_fwd_split: per-item partial outputs and LSEs into ``workspace``."""
+    import torch
+    _require(q, "q", torch.bfloat16, 4)
+    dev = q.device
+    _require(kv_cache, "kv_cache", torch.bfloat16, 3, dev)
+    _require(block_table, "block_table", torch.int32, 2, dev)
+    _require(seqlens, "seqlens", torch.int32, 1, dev)
+    _require(workspace, "workspace", torch.uint8, 1, dev)
+    b, s_q, h, _ = q.shape
+    _check("mla_decode_fwd_split", lib().mla_decode_fwd_split(
+        q.data_ptr(), kv_cache.data_ptr(), block_table.data_ptr(), block_table.shape[1], seqlens.data_ptr(),
+        b, s_q, h, kv_cache.shape[0], kv_cache.shape[1], float(softmax_scale), int(bool(causal)),
+        workspace.data_ptr(), workspace.numel(), _stream(stream)))
+
+
+def fwd_combine(seqlens, bt_stride: int, s_q: int, num_heads: int, workspace, out, lse, stream=None) -> None:
+    """mla_decode_fwd_combine: merge the partials in ``workspace`` into ``out`` and ``lse``."""
+    import torch
+    _require(seqlens, "seqlens", torch.int32, 1)
+    dev = seqlens.device
+    _require(workspace, "workspace", torch.uint8, 1, dev)
+    _require(out, "out", torch.bfloat16, 4, dev)
+    _require(lse, "lse", torch.float32, 3, dev)
+    b = seqlens.shape[0]
+    if tuple(out.shape) != (b, s_q, num_heads, D_V) or tuple(lse.shape) != (b, s_q, num_heads):
+        raise ValueError("out must be [b, s_q, h, 512] and lse [b, s_q, h]")
+    _check("mla_decode_fwd_combine", lib().mla_decode_fwd_combine(
+        seqlens.data_ptr(), int(bt_stride), b, int(s_q), int(num_heads), workspace.data_ptr(), workspace.numel(),
+        out.data_ptr(), lse.data_ptr(), _stream(stream)))
+
+
+def decode(q, kv_cache, block_table, seqlens, softmax_scale: float, causal: bool = False, workspace=None,
+           out=None, lse=None, stream=None, replan: bool = True):
+    """Allocate what is missing, then plan (unless ``replan`` is False) and run one decode step."""
+    import torch
+    b, s_q, h, _ = q.shape
+    if workspace is None:
+        workspace = torch.empty(workspace_size(b, s_q, h), dtype=torch.uint8, device=q.device)
+        replan = True
+    if out is None:
+        out = torch.empty((b, s_q, h, D_V), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((b, s_q, h), dtype=torch.float32, device=q.device)
+    if replan:
+        plan(seqlens, s_q, h, workspace, stream)
+    fwd(q, kv_cache, block_table, seqlens, softmax_scale, causal, workspace, out, lse, stream)
+    return out, lse

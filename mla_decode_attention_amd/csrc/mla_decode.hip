@@ -1,0 +1,290 @@
+// Host side of the C ABI declared in include/mla_decode.h: argument validation (before any HIP
+// call), per-device launch geometry, workspace sizing and the kernel launches.
+#include "mla_decode.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+
+#include "mla_decode_kernels.h"
+
+namespace {
+
+using namespace mla;
+
+// Launch configurations by query rows per sequence (s_q * heads).
+//                                 waves  row-blocks/group  tile tokens  stages/group
+using CfgR16 = SplitCfg<4, 1, 16, 2>;   // 4 independent waves, 2 x 18 KiB stages each
+using CfgR32 = SplitCfg<4, 2, 32, 2>;   // 2 groups x 2 waves, 2 x 36 KiB stages per group
+using CfgR64 = SplitCfg<4, 4, 32, 4>;   // 1 group of 4 waves, 4 x 36 KiB stages
+using CfgR128 = SplitCfg<8, 8, 32, 4>;  // 1 group of 8 waves, 4 x 36 KiB stages (R = 256: 2 row groups)
+
+enum CfgId { kR16 = 0, kR32, kR64, kR128, kNumCfg };
+
+struct LaunchGeom {
+    CfgId cfg;
+    int row_groups;   // grid.y
+    int threads;
+    int lds_bytes;
+};
+
+bool geom_for(int s_q, int heads, LaunchGeom* g)
+{
+    const int rows = s_q * heads;
+    switch (rows) {
+    case 16: *g = {kR16, 1, CfgR16::THREADS, CfgR16::LDS_BYTES}; return true;
+    case 32: *g = {kR32, 1, CfgR32::THREADS, CfgR32::LDS_BYTES}; return true;
+    case 64: *g = {kR64, 1, CfgR64::THREADS, CfgR64::LDS_BYTES}; return true;
+    case 128: *g = {kR128, 1, CfgR128::THREADS, CfgR128::LDS_BYTES}; return true;
+    case 256: *g = {kR128, 2, CfgR128::THREADS, CfgR128::LDS_BYTES}; return true;
+    default: return false;
+    }
+}
+
+const void* split_fn(CfgId c)
+{
+    switch (c) {
+    case kR16: return reinterpret_cast<const void*>(&split_kernel<CfgR16>);
+    case kR32: return reinterpret_cast<const void*>(&split_kernel<CfgR32>);
+    case kR64: return reinterpret_cast<const void*>(&split_kernel<CfgR64>);
+    default: return reinterpret_cast<const void*>(&split_kernel<CfgR128>);
+    }
+}
+
+struct DeviceInfo {
+    bool ready = false;
+    int status = MLA_OK;
+    int num_cu = 0;
+    int occupancy[kNumCfg] = {};
+};
+
+constexpr int kMaxDevices = 64;
+std::mutex g_mutex;
+DeviceInfo g_dev[kMaxDevices];
+
+int device_info(const DeviceInfo** out)
+{
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
+        (void)hipGetLastError();
+        return MLA_ERR_NO_DEVICE;
+    }
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return MLA_ERR_NO_DEVICE;
+    }
+    std::lock_guard<std::mutex> lock(g_mutex);
+    DeviceInfo& d = g_dev[dev];
+    if (!d.ready) {
+        d.ready = true;
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            d.status = MLA_ERR_NO_DEVICE;
+        } else if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+            d.status = MLA_ERR_NO_DEVICE;   // the code objects are built for gfx950 only
+        } else {
+            d.num_cu = prop.multiProcessorCount;
+            static const int threads[kNumCfg] = {CfgR16::THREADS, CfgR32::THREADS, CfgR64::THREADS,
+                                                 CfgR128::THREADS};
+            static const int lds[kNumCfg] = {CfgR16::LDS_BYTES, CfgR32::LDS_BYTES, CfgR64::LDS_BYTES,
+                                             CfgR128::LDS_BYTES};
+            for (int c = 0; c < kNumCfg; ++c) {
+                const void* fn = split_fn(static_cast<CfgId>(c));
+                int occ = 0;
+                if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds[c]) != hipSuccess ||
+                    hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, threads[c], lds[c]) != hipSuccess ||
+                    occ < 1) {
+                    (void)hipGetLastError();
+                    d.status = MLA_ERR_HIP;
+                    break;
+                }
+                d.occupancy[c] = occ;
+            }
+        }
+    }
+    *out = &d;
+    return d.status;
+}
+
+bool heads_ok(int s_q, int heads)
+{
+    return (s_q == 1 || s_q == 2) && (heads == 16 || heads == 32 || heads == 64 || heads == 128);
+}
+
+// Work items the split kernel can take per row group: one per resident workgroup slot, plus one
+// per sequence for the rounding of per-sequence split counts.
+int item_capacity(const DeviceInfo& d, const LaunchGeom& g, int batch)
+{
+    int gx = d.num_cu * d.occupancy[g.cfg] / g.row_groups;
+    if (gx < 1) gx = 1;
+    return gx + batch;
+}
+
+int gx_of(const DeviceInfo& d, const LaunchGeom& g)
+{
+    int gx = d.num_cu * d.occupancy[g.cfg] / g.row_groups;
+    return gx < 1 ? 1 : gx;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int mla_decode_workspace_size(int batch, int s_q, int num_heads, size_t* bytes)
+{
+    if (!bytes || batch < 1) return MLA_ERR_INVALID_ARG;
+    if (!heads_ok(s_q, num_heads)) return MLA_ERR_UNSUPPORTED;
+    const DeviceInfo* d = nullptr;
+    const int st = device_info(&d);
+    if (st != MLA_OK) return st;
+    LaunchGeom g;
+    geom_for(s_q, num_heads, &g);
+    *bytes = ws_layout(batch, s_q * num_heads, item_capacity(*d, g, batch)).total;
+    return MLA_OK;
+}
+
+int mla_decode_plan(const int32_t* seqlens, int batch, int s_q, int num_heads, void* workspace,
+                    size_t workspace_bytes, void* stream)
+{
+    if (!seqlens || !workspace || batch < 1) return MLA_ERR_INVALID_ARG;
+    if (!aligned(workspace, 256) || !aligned(seqlens, 4)) return MLA_ERR_INVALID_ARG;
+    if (!heads_ok(s_q, num_heads)) return MLA_ERR_UNSUPPORTED;
+    const DeviceInfo* d = nullptr;
+    const int st = device_info(&d);
+    if (st != MLA_OK) return st;
+    LaunchGeom g;
+    geom_for(s_q, num_heads, &g);
+    const int cap = item_capacity(*d, g, batch);
+    if (workspace_bytes < ws_layout(batch, s_q * num_heads, cap).total) return MLA_ERR_WORKSPACE_TOO_SMALL;
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, static_cast<hipStream_t>(stream), seqlens,
+                       batch, s_q, num_heads, s_q * num_heads, gx_of(*d, g), cap, static_cast<char*>(workspace));
+    return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+namespace {
+
+int prepare_fwd(const void* q, const void* kv_cache, const int32_t* block_table, int bt_stride,
+                const int32_t* seqlens, int batch, int s_q, int num_heads, int num_pages, int page_size,
+                float softmax_scale, int causal, void* workspace, size_t workspace_bytes, void* out, float* lse,
+                bool need_inputs, bool need_outputs, FwdArgs* a, LaunchGeom* g)
+{
+    if (!seqlens || !workspace) return MLA_ERR_INVALID_ARG;
+    if (need_inputs && (!q || !kv_cache || !block_table)) return MLA_ERR_INVALID_ARG;
+    if (need_outputs && (!out || !lse)) return MLA_ERR_INVALID_ARG;
+    if (batch < 1 || bt_stride < 1) return MLA_ERR_INVALID_ARG;
+    if (need_inputs && num_pages < 1) return MLA_ERR_INVALID_ARG;
+    if (need_inputs && (!std::isfinite(softmax_scale) || (causal != 0 && causal != 1))) return MLA_ERR_INVALID_ARG;
+    if (!aligned(workspace, 256) || !aligned(seqlens, 4)) return MLA_ERR_INVALID_ARG;
+    if (need_inputs && (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(block_table, 4)))
+        return MLA_ERR_INVALID_ARG;
+    if (need_outputs && (!aligned(out, 8) || !aligned(lse, 4))) return MLA_ERR_INVALID_ARG;
+    if (!heads_ok(s_q, num_heads) || (need_inputs && page_size != MLA_DECODE_PAGE_SIZE)) return MLA_ERR_UNSUPPORTED;
+    const DeviceInfo* d = nullptr;
+    const int st = device_info(&d);
+    if (st != MLA_OK) return st;
+    geom_for(s_q, num_heads, g);
+    const int rows = s_q * num_heads;
+    const int cap = item_capacity(*d, *g, batch);
+    if (workspace_bytes < ws_layout(batch, rows, cap).total) return MLA_ERR_WORKSPACE_TOO_SMALL;
+    a->q = static_cast<const uint16_t*>(q);
+    a->cache = static_cast<const uint16_t*>(kv_cache);
+    a->block_table = block_table;
+    a->seqlens = seqlens;
+    a->ws = static_cast<char*>(workspace);
+    a->out = static_cast<uint16_t*>(out);
+    a->lse = lse;
+    a->num_pages = num_pages;
+    a->bt_stride = bt_stride;
+    a->batch = batch;
+    a->s_q = s_q;
+    a->heads = num_heads;
+    a->rows = rows;
+    a->capacity = cap;
+    a->scale_log2 = softmax_scale * kLog2e;
+    a->causal = causal;
+    return MLA_OK;
+}
+
+int launch_split(const FwdArgs& a, const LaunchGeom& g, hipStream_t s)
+{
+    const dim3 grid(a.capacity, g.row_groups);
+    switch (g.cfg) {
+    case kR16: hipLaunchKernelGGL(split_kernel<CfgR16>, grid, dim3(g.threads), g.lds_bytes, s, a); break;
+    case kR32: hipLaunchKernelGGL(split_kernel<CfgR32>, grid, dim3(g.threads), g.lds_bytes, s, a); break;
+    case kR64: hipLaunchKernelGGL(split_kernel<CfgR64>, grid, dim3(g.threads), g.lds_bytes, s, a); break;
+    default: hipLaunchKernelGGL(split_kernel<CfgR128>, grid, dim3(g.threads), g.lds_bytes, s, a); break;
+    }
+    return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int launch_combine(const FwdArgs& a, hipStream_t s)
+{
+    const int blocks = (a.batch * a.rows + 1) / 2;
+    hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(kCombineThreads), 0, s, a);
+    return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+}  // namespace
+
+int mla_decode_fwd(const void* q, const void* kv_cache, const int32_t* block_table, int bt_stride,
+                   const int32_t* seqlens, int batch, int s_q, int num_heads, int num_pages, int page_size,
+                   float softmax_scale, int causal, void* workspace, size_t workspace_bytes, void* out,
+                   float* lse, void* stream)
+{
+    FwdArgs a;
+    LaunchGeom g;
+    int st = prepare_fwd(q, kv_cache, block_table, bt_stride, seqlens, batch, s_q, num_heads, num_pages, page_size,
+                         softmax_scale, causal, workspace, workspace_bytes, out, lse, true, true, &a, &g);
+    if (st != MLA_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = launch_split(a, g, s);
+    if (st != MLA_OK) return st;
+    return launch_combine(a, s);
+}
+
+int mla_decode_fwd_split(const void* q, const void* kv_cache, const int32_t* block_table, int bt_stride,
+                         const int32_t* seqlens, int batch, int s_q, int num_heads, int num_pages, int page_size,
+                         float softmax_scale, int causal, void* workspace, size_t workspace_bytes, void* stream)
+{
+    FwdArgs a;
+    LaunchGeom g;
+    const int st = prepare_fwd(q, kv_cache, block_table, bt_stride, seqlens, batch, s_q, num_heads, num_pages,
+                               page_size, softmax_scale, causal, workspace, workspace_bytes, nullptr, nullptr, true,
+                               false, &a, &g);
+    if (st != MLA_OK) return st;
+    return launch_split(a, g, static_cast<hipStream_t>(stream));
+}
+
+int mla_decode_fwd_combine(const int32_t* seqlens, int bt_stride, int batch, int s_q, int num_heads,
+                           void* workspace, size_t workspace_bytes, void* out, float* lse, void* stream)
+{
+    FwdArgs a;
+    LaunchGeom g;
+    const int st = prepare_fwd(nullptr, nullptr, nullptr, bt_stride, seqlens, batch, s_q, num_heads, 1,
+                               MLA_DECODE_PAGE_SIZE, 1.f, 0, workspace, workspace_bytes, out, lse, false, true, &a,
+                               &g);
+    if (st != MLA_OK) return st;
+    return launch_combine(a, static_cast<hipStream_t>(stream));
+}
+
+const char* mla_decode_status_string(int status)
+{
+    switch (status) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG: null pointer, bad size, alignment or non-finite scale";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: heads must be 16/32/64/128, s_q 1 or 2, page size 64";
+    case MLA_ERR_WORKSPACE_TOO_SMALL: return "MLA_ERR_WORKSPACE_TOO_SMALL: see mla_decode_workspace_size";
+    case MLA_ERR_NO_DEVICE: return "MLA_ERR_NO_DEVICE: no usable gfx950 HIP device";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP: a HIP runtime call failed";
+    default: return "unknown mla_status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,191 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle, element by element."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from mla_decode_attention_amd import workloads
+from mla_decode_attention_amd.inputs import make_case
+
+from gpu_helpers import log, parity, run_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mla_decode_attention_amd as mla
+    mla.lib()
+    return torch.device("cuda:0")
+
+
+def full_parity(case, dev, what=None):
+    what = what or case.name
+    log(f"case {what}: b={case.batch} s_q={case.s_q} h={case.heads} L={case.seqlens.tolist()[:6]} "
+        f"causal={case.causal} pages={case.num_pages}")
+    o, l = run_gpu(case, dev)
+    ro, rl = oracle.mla_decode(case.q, case.cache, case.block_table, case.seqlens, case.softmax_scale, case.causal)
+    return parity(o, l, ro, rl, what)
+
+
+@pytest.mark.parametrize("name", ["tiny_b1_h16_L256", "paged_b16_h16_L4096", "mtp_b16_h16_sq2_L8K-16K"])
+def test_workload_full(dev, name):
+    full_parity(workloads.build(name), dev)
+
+
+@pytest.mark.parametrize("name,n_rows", [("long_b16_h16_L65536", 48), ("allheads_b8_h128_L32768", 64)])
+def test_workload_sampled_rows(dev, name, n_rows):
+    """Full-size workloads in the benchmark's launch configuration; the oracle computes sampled rows."""
+    case = workloads.build(name)
+    log(f"case {name}: generated, running on GPU")
+    o, l = run_gpu(case, dev)
+    rng = np.random.default_rng(99)
+    rows = np.sort(rng.choice(case.rows, n_rows, replace=False))
+    ro, rl = oracle.mla_decode(case.q, case.cache, case.block_table, case.seqlens, case.softmax_scale,
+                               case.causal, rows=rows)
+    parity(o.reshape(case.rows, -1)[rows], l.reshape(-1)[rows], ro, rl, f"{name} ({n_rows} sampled rows)")
+
+
+RAGGED = [1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 129, 1000, 4097]
+
+
+@pytest.mark.parametrize("heads,s_q,causal", [(16, 1, False), (16, 2, True), (16, 2, False), (32, 1, False),
+                                             (32, 2, True), (64, 1, False), (64, 2, True), (128, 1, False),
+                                             (128, 2, True)])
+def test_ragged_lengths_all_row_configs(dev, heads, s_q, causal):
+    lens = RAGGED if heads <= 32 else RAGGED[:10] + [700]
+    case = make_case(f"ragged_h{heads}_sq{s_q}", batch=len(lens), s_q=s_q, heads=heads, seqlen=lens, seed=31,
+                     causal=causal, pool_pages=sum((L + 63) // 64 for L in lens) + 5, table_slack=3)
+    full_parity(case, dev)
+
+
+def test_empty_and_single_key_sequences(dev):
+    case = make_case("empty_mix", batch=5, s_q=2, heads=16, seqlen=[0, 1, 2, 0, 70], seed=32, causal=True)
+    full_parity(case, dev)
+
+
+def test_zero_query_gives_mean_value(dev):
+    case = make_case("zero_q", batch=2, s_q=1, heads=16, seqlen=[300, 4000], seed=33, zero_q=True)
+    o, l = run_gpu(case, dev)
+    np.testing.assert_allclose(l, np.log(case.seqlens.astype(np.float64))[:, None, None].repeat(16, 2),
+                               rtol=1e-6)
+    full_parity(case, dev)
+
+
+def test_outlier_rows_softmax_max_tracking(dev):
+    case = make_case("outliers", batch=4, s_q=2, heads=32, seqlen=(3000, 9000), seed=34, causal=True,
+                     outlier_frac=0.01, outlier_scale=8.0)
+    full_parity(case, dev)
+
+
+def test_deterministic_for_a_plan(dev):
+    import torch
+
+    import mla_decode_attention_amd as mla
+    case = make_case("det", batch=3, s_q=1, heads=16, seqlen=[5000, 130, 2048], seed=35)
+    q, cache, bt, sl = to_device(case, dev)
+    out1, lse1 = mla.decode(q, cache, bt, sl, case.softmax_scale, False)
+    out2, lse2 = out1.clone(), lse1.clone()
+    out1.zero_()
+    mla.fwd(q, cache, bt, sl, case.softmax_scale, False, *_workspace_for(mla, case, sl, dev), out1, lse1)
+    torch.cuda.synchronize()
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16)) and torch.equal(lse1, lse2)
+
+
+def _workspace_for(mla, case, sl, dev):
+    import torch
+    ws = torch.empty(mla.workspace_size(case.batch, case.s_q, case.heads), dtype=torch.uint8, device=dev)
+    mla.plan(sl, case.s_q, case.heads, ws)
+    return (ws,)
+
+
+def test_bad_page_and_mismatched_plan_give_nan_not_fault(dev):
+    import torch
+
+    import mla_decode_attention_amd as mla
+    case = make_case("badpage", batch=3, s_q=1, heads=16, seqlen=[200, 300, 100], seed=36)
+    q, cache, bt, sl = to_device(case, dev)
+    bt_bad = bt.clone()
+    bt_bad[1, 2] = case.num_pages + 7          # out of the pool
+    out, lse = mla.decode(q, cache, bt_bad, sl, case.softmax_scale, False)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy()
+    l = lse.cpu().numpy()
+    assert np.isnan(o[1]).all() and np.isnan(l[1]).all()
+    ro, rl = oracle.mla_decode(case.q, case.cache, case.block_table, case.seqlens, case.softmax_scale, False)
+    parity(o[[0, 2]], l[[0, 2]], ro[[0, 2]], rl[[0, 2]], "sequences beside a bad page")
+    # plan made for other seqlens
+    ws = torch.empty(mla.workspace_size(3, 1, 16), dtype=torch.uint8, device=dev)
+    mla.plan(sl + 1, 1, 16, ws)
+    out2 = torch.empty_like(out)
+    lse2 = torch.empty_like(lse)
+    mla.fwd(q, cache, bt, sl, case.softmax_scale, False, ws, out2, lse2)
+    torch.cuda.synchronize()
+    assert torch.isnan(lse2).all()
+    # plan made for another head count: the whole batch is NaN
+    ws3 = torch.empty(mla.workspace_size(3, 1, 32), dtype=torch.uint8, device=dev)
+    mla.plan(sl, 1, 32, ws3)
+    mla.fwd(q, cache, bt, sl, case.softmax_scale, False, ws3, out2, lse2)
+    torch.cuda.synchronize()
+    assert torch.isnan(lse2).all() and torch.isnan(out2.float()).all()
+
+
+def test_workspace_too_small_is_reported(dev):
+    import torch
+
+    import mla_decode_attention_amd as mla
+    case = make_case("ws", batch=2, s_q=1, heads=16, seqlen=[64, 64], seed=37)
+    q, cache, bt, sl = to_device(case, dev)
+    need = mla.workspace_size(2, 1, 16)
+    ws = torch.empty(need - 256, dtype=torch.uint8, device=dev)
+    with pytest.raises(mla.MlaDecodeError) as e:
+        mla.plan(sl, 1, 16, ws)
+    assert e.value.status == -3
+
+
+def test_plan_covers_every_page_once(dev):
+    """Read the plan back: items tile each sequence's pages exactly once, in balanced chunks."""
+    import torch
+
+    import mla_decode_attention_amd as mla
+    lens = [0, 1, 64, 65, 5000, 65536, 12345, 3]
+    sl = torch.tensor(lens, dtype=torch.int32, device=dev)
+    for s_q, heads in [(1, 16), (2, 16), (1, 128), (2, 128)]:
+        ws = torch.zeros(mla.workspace_size(len(lens), s_q, heads), dtype=torch.uint8, device=dev)
+        mla.plan(sl, s_q, heads, ws)
+        torch.cuda.synchronize()
+        w = ws.cpu().numpy()
+        hdr = w[:64].view(np.int32)
+        assert hdr[0] == 0x4D4C4131 and hdr[1] == len(lens) and hdr[2] == s_q and hdr[3] == heads
+        n_items, cap, rows = int(hdr[4]), int(hdr[5]), int(hdr[6])
+        assert rows == s_q * heads and n_items <= cap
+
+        def a256(x):
+            return (x + 255) & ~255
+        off = a256(64)
+        off_len = off
+        off = a256(off + 4 * len(lens))
+        off_bs = off
+        off = a256(off + 4 * (len(lens) + 1))
+        off_items = off
+        assert w[off_len:off_len + 4 * len(lens)].view(np.int32).tolist() == lens
+        bs = w[off_bs:off_bs + 4 * (len(lens) + 1)].view(np.int32)
+        items = w[off_items:off_items + 16 * n_items].view(np.int32).reshape(-1, 4)
+        assert bs[0] == 0 and bs[-1] == n_items and np.all(np.diff(bs) >= 0)
+        sizes = []
+        for b, L in enumerate(lens):
+            its = items[bs[b]:bs[b + 1]]
+            pages = (L + 63) // 64
+            assert (its[:, 0] == b).all()
+            assert its[:, 3].tolist() == list(range(len(its)))
+            covered = [p for it in its for p in range(it[1], it[2])]
+            assert covered == list(range(pages)), (b, L)
+            sizes += (its[:, 2] - its[:, 1]).tolist()
+        total = sum((L + 63) // 64 for L in lens)
+        chunk = -(-total // (cap - len(lens)))
+        assert max(sizes) <= max(chunk, 1)
+        log(f"plan s_q={s_q} h={heads}: {n_items} items (capacity {cap}), chunk {chunk}, sizes {min(sizes)}..{max(sizes)}")
