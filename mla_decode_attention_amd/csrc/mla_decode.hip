@@ -16,11 +16,14 @@ namespace {
 using namespace mla;
 
 // Launch configurations by query rows per sequence (s_q * heads).
-//                                 waves  row-blocks/group  tile tokens  stages/group
-using CfgR16 = SplitCfg<4, 1, 16, 2>;   // 4 independent waves, 2 x 18 KiB stages each
-using CfgR32 = SplitCfg<4, 2, 32, 2>;   // 2 groups x 2 waves, 2 x 36 KiB stages per group
-using CfgR64 = SplitCfg<4, 4, 32, 4>;   // 1 group of 4 waves, 4 x 36 KiB stages
-using CfgR128 = SplitCfg<8, 8, 32, 4>;  // 1 group of 8 waves, 4 x 36 KiB stages (R = 256: 2 row groups)
+// A wave owns one 16-row block (or, with DS > 1, a 512/DS-dim segment of it).  For 16-32 rows,
+// four waves per CU with one 18-36 KiB tile in flight each stream as fast as eight (measured),
+// so the smaller-register eight-wave form is kept for wider row counts only.
+//                         waves  row-blocks  segments  tile tokens  LDS stages  register tiles
+using CfgR16 = SplitCfg<4, 1, 1, 16, 1, 1>;    // 4 independent waves, one 18 KiB tile each
+using CfgR32 = SplitCfg<4, 2, 1, 32, 2, 1>;    // 2 groups x 2 waves, 2 x 36 KiB stages per group
+using CfgR64 = SplitCfg<4, 4, 1, 32, 2, 1>;    // 1 group of 4 waves, 2 x 36 KiB stages
+using CfgR128 = SplitCfg<8, 8, 1, 64, 2, 1>;   // 1 group of 8 waves x 72 KiB tiles (R = 256: 2 row groups)
 
 enum CfgId { kR16 = 0, kR32, kR64, kR128, kNumCfg };
 
@@ -226,8 +229,7 @@ int launch_split(const FwdArgs& a, const LaunchGeom& g, hipStream_t s)
 
 int launch_combine(const FwdArgs& a, hipStream_t s)
 {
-    const int blocks = (a.batch * a.rows + 1) / 2;
-    hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(kCombineThreads), 0, s, a);
+    hipLaunchKernelGGL(combine_kernel, dim3(a.batch * a.rows), dim3(kCombineThreads), 0, s, a);
     return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

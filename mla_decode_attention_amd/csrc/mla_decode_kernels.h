@@ -27,11 +27,13 @@ constexpr int kDv = 512;
 constexpr int kPage = 64;
 constexpr int kRowBytes = kDk * 2;          // 1152
 constexpr int kChunksPerRow = kRowBytes / 16;  // 72 chunks of 16 B
+constexpr int kLdsRow = kRowBytes + 16;        // LDS row stride: 1168 B = 73 chunks (odd), see below
 constexpr int kKSteps = kDk / 32;           // 18 score MFMA k-steps of 32
 constexpr int kDTiles = kDv / 16;           // 32 output tiles of 16 dims
 constexpr int kPlanMagic = 0x4D4C4131;      // "MLA1"
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kNonTemporal = 2;             // buffer-load cache policy: stream the cache through
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -158,42 +160,50 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(const int32_t* __res
 //
 // A workgroup takes one work item (sequence b, page range) and one row group (RB blocks of 16
 // query rows; rows are ordered [s_q][heads]).  Its NW waves form NG = NW/RB wave groups; each
-// group streams its own share of the item's TT-token tiles (round robin) through NSG LDS
-// stages, the RB waves of a group sharing each stage, one 16-row block per wave.
+// group streams its own share of the item's TT-token tiles (round robin) through NS LDS stages,
+// the RB waves of a group sharing each stage, one 16-row block per wave.
 //
-// Tiles move HBM -> LDS with buffer_load_dwordx4 ... lds (16 B per lane, no VGPR staging),
-// issued from inline asm so that the compiler does not put a vmcnt(0) before every LDS read;
-// the waits are explicit vmcnt counts.  The buffer resource of a tile ends at the sequence's
-// last valid row, so rows past L_b load as zeros and never reach the value contraction.
+// Tiles move HBM -> VGPR -> LDS: every load instruction of a wave reads one contiguous KiB of
+// the tile (16 B per lane, the access that streams fastest), NR tiles per wave are in flight in
+// registers, and each arrived tile is stored to LDS just before it is needed.  The buffer
+// resource of a tile ends at the sequence's last valid row, so rows past L_b load as zeros and
+// never reach the value contraction (0 * NaN would poison it).
 //
-// LDS tile layout: rows of 1152 B; within each row the 16-B chunk c is stored at chunk
-// c ^ (row & 7) (a permutation inside aligned 128-B groups), which spreads the 16 rows that a
-// K-operand read touches over distinct bank groups.  The swizzle is applied by choosing which
-// global chunk each lane loads, so every DMA still reads a contiguous 1 KiB of HBM.
+// LDS tile layout: row r of a tile starts at r * 1168 B (16 B of padding per 1152-B row).  An
+// odd number of 16-B chunks per row puts the 16 rows that one K-operand read touches, and the
+// 4 rows of each transposed V read, on distinct bank groups.
 // =============================================================================================
-template <int NW_, int RB_, int TT_, int NSG_>
+template <int NW_, int RB_, int DS_, int TT_, int NS_, int NR_>
 struct SplitCfg {
     static constexpr int NW = NW_;            // waves per workgroup
-    static constexpr int RB = RB_;            // 16-row blocks per wave group (= waves per group)
-    static constexpr int NG = NW / RB;        // wave groups
-    static constexpr int TT = TT_;            // tokens per tile (16 or 32)
-    static constexpr int NSG = NSG_;          // LDS stages per group
+    static constexpr int RB = RB_;            // 16-row blocks per wave group
+    static constexpr int DS = DS_;            // output segments: waves sharing a row block, each
+                                              // accumulating 512/DS of the value dims
+    static constexpr int GW = RB * DS;        // waves per group
+    static constexpr int NG = NW / GW;        // wave groups
+    static constexpr int TT = TT_;            // tokens per tile (16, 32 or 64)
+    static constexpr int NS = NS_;            // LDS stages per group
+    static constexpr int NR = NR_;            // tiles in flight in registers per wave
     static constexpr int NST = TT / 16;       // 16-token sub-tiles per tile
-    static constexpr int TILE_BYTES = TT * kRowBytes;
-    static constexpr int UNITS = TILE_BYTES / 1024;          // 1-KiB DMA units per tile
-    static constexpr int NPW = (UNITS + RB - 1) / RB;        // DMA instructions per wave per tile
-    static constexpr int STAGE_BYTES = TILE_BYTES;
-    static constexpr int DUMMY_OFF = NG * NSG * STAGE_BYTES; // 1 KiB sink for padding DMAs
-    static constexpr int LDS_BYTES = DUMMY_OFF + ((UNITS % RB) ? 1024 : 0);
-    static constexpr int THREADS = NW * 64;
-    static_assert(NW % RB == 0, "waves must split into whole groups");
-    static_assert(TT == 16 || TT == 32, "tile is one or two MFMA token blocks");
-    static_assert(TILE_BYTES % 1024 == 0, "tile must be whole DMA units");
-    static_assert(NSG >= 2 && NSG <= 4, "2..4 stages");
-    static_assert((NSG - 2) * NPW < 64, "outstanding DMAs must fit the vmcnt field");
+    static constexpr int DTW = kDTiles / DS;  // 16-dim output tiles per wave
+    static constexpr int TILE_BYTES = TT * kRowBytes;        // in HBM
+    static constexpr int LDS_TILE = TT * kLdsRow;            // in LDS (padded rows)
+    static constexpr int UNITS = TILE_BYTES / 1024;          // 1-KiB load units per tile
+    static constexpr int NPW = UNITS / GW;                   // load units per wave per tile
+    static constexpr int STAGE_BYTES = NG * NS * LDS_TILE;
     // merge scratch (reuses the stage area): m, l per wave + fp32 accumulators
-    static constexpr int MERGE_BYTES = NW * (2 * 16 * 4 + 16 * kDv * 4);
-    static_assert(NG == 1 || MERGE_BYTES <= LDS_BYTES, "merge scratch must fit");
+    static constexpr int MERGE_BYTES = NG > 1 ? NW * (2 * 16 * 4 + 16 * (kDv / DS) * 4) : 0;
+    static constexpr int LDS_BYTES = STAGE_BYTES > MERGE_BYTES ? STAGE_BYTES : MERGE_BYTES;
+    static constexpr int THREADS = NW * 64;
+    static_assert(NW % GW == 0, "waves must split into whole groups");
+    static_assert(DS == 1 || DS == 2 || DS == 4, "output segments");
+    static_assert(TT == 16 || TT == 32 || TT == 64, "tile is 1, 2 or 4 MFMA token blocks");
+    static_assert(TILE_BYTES % 1024 == 0, "tile must be whole load units");
+    static_assert(NPW * GW == UNITS && NPW % 9 == 0, "each wave loads whole 8-row groups (9 KiB)");
+    static_assert(NR == 1 || NR == 2, "one or two tiles in flight per wave");
+    static_assert(GW == 1 || NS == 2, "shared stages need double buffering");
+    static_assert(NS == 1 || NS == 2, "one or two stages");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
 struct FwdArgs {
@@ -211,61 +221,29 @@ struct FwdArgs {
     int causal;
 };
 
-#define MLA_VMCNT_CASE(n) \
-    case n: asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory"); break;
-// Wait until at most n of this wave's vector-memory operations are outstanding.  n is
-// wave-uniform; s_waitcnt needs an immediate, hence the switch (values above 39 wait for all).
-__device__ inline void wait_vmcnt_le(int n)
-{
-    switch (n) {
-        MLA_VMCNT_CASE(1) MLA_VMCNT_CASE(2) MLA_VMCNT_CASE(3) MLA_VMCNT_CASE(4) MLA_VMCNT_CASE(5)
-        MLA_VMCNT_CASE(6) MLA_VMCNT_CASE(7) MLA_VMCNT_CASE(8) MLA_VMCNT_CASE(9) MLA_VMCNT_CASE(10)
-        MLA_VMCNT_CASE(11) MLA_VMCNT_CASE(12) MLA_VMCNT_CASE(13) MLA_VMCNT_CASE(14) MLA_VMCNT_CASE(15)
-        MLA_VMCNT_CASE(16) MLA_VMCNT_CASE(17) MLA_VMCNT_CASE(18) MLA_VMCNT_CASE(19) MLA_VMCNT_CASE(20)
-        MLA_VMCNT_CASE(21) MLA_VMCNT_CASE(22) MLA_VMCNT_CASE(23) MLA_VMCNT_CASE(24) MLA_VMCNT_CASE(25)
-        MLA_VMCNT_CASE(26) MLA_VMCNT_CASE(27) MLA_VMCNT_CASE(28) MLA_VMCNT_CASE(29) MLA_VMCNT_CASE(30)
-        MLA_VMCNT_CASE(31) MLA_VMCNT_CASE(32) MLA_VMCNT_CASE(33) MLA_VMCNT_CASE(34) MLA_VMCNT_CASE(35)
-        MLA_VMCNT_CASE(36) MLA_VMCNT_CASE(37) MLA_VMCNT_CASE(38) MLA_VMCNT_CASE(39)
-    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-    }
-}
-#undef MLA_VMCNT_CASE
-
-// One 16-B-per-lane DMA from a buffer resource into LDS at m0 + 16*lane.
-__device__ inline void dma16(i32x4 rsrc, uint32_t voff, uint32_t lds_addr)
-{
-    asm volatile(
-        "s_waitcnt lgkmcnt(0)\n\t"
-        "s_mov_b32 m0, %2\n\t"
-        "s_nop 0\n\t"
-        "buffer_load_dwordx4 %0, %1, 0 offen lds"
-        :
-        : "v"(voff), "s"(rsrc), "s"(lds_addr)
-        : "memory");
-}
-
-__device__ inline uint32_t lds_u32(const void* p)
-{
-    return (uint32_t)(uintptr_t)(const MLA_LDS char*)p;
-}
-
 __device__ inline const MLA_LDS i16x4* lds_i16x4(const void* p)
 {
     return (const MLA_LDS i16x4*)(const MLA_LDS char*)p;
 }
 
+// Reductions across the four 16-lane groups of a wave (lanes l, l^16, l^32, l^48), with the
+// gfx950 row-swap permutes: permlane16_swap exchanges 16-lane rows 0<->1 and 2<->3 between its
+// two results, permlane32_swap the 32-lane halves, so op(first, second) combines each lane with
+// its partner.
 __device__ inline float wave_max_groups(float v)
 {
-    v = fmaxf(v, __shfl_xor(v, 16));
-    v = fmaxf(v, __shfl_xor(v, 32));
-    return v;
+    auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
 
 __device__ inline float wave_sum_groups(float v)
 {
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    return v;
+    auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+    auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
 __device__ inline uint16_t f32_to_bf16_rne(float f)
@@ -276,6 +254,11 @@ __device__ inline uint16_t f32_to_bf16_rne(float f)
     return (uint16_t)(u >> 16);
 }
 
+template <int B>
+struct Idx {
+    static constexpr int value = B;
+};
+
 template <class C>
 __global__ void __launch_bounds__(C::THREADS) split_kernel(FwdArgs a)
 {
@@ -283,8 +266,11 @@ __global__ void __launch_bounds__(C::THREADS) split_kernel(FwdArgs a)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int gi = wave / C::RB;            // wave group
-    const int rbl = wave % C::RB;           // row block within the group
+    const int gi = wave / C::GW;            // wave group
+    const int wg = wave % C::GW;            // wave within the group
+    const int rbl = wg / C::DS;             // row block within the group
+    const int dsi = wg % C::DS;             // output segment: value dims [512 dsi / DS, ...)
+    const int dt0 = dsi * C::DTW;           // first 16-dim output tile of this wave
     const int lr = lane & 15;               // lane's query row within its block (MFMA column)
     const int lg = lane >> 4;               // lane group (MFMA k / row quad)
 
@@ -324,40 +310,35 @@ __global__ void __launch_bounds__(C::THREADS) split_kernel(FwdArgs a)
 #pragma unroll
         for (int j = 0; j < kKSteps; ++j)
             qop[j] = *reinterpret_cast<const bf16x8*>(qrow + 32 * j + 8 * lg);
-        // Consume Q here so the compiler's own vmcnt waits for these loads land before the
-        // tile loop, not inside it (where they would also wait for the in-flight tile DMAs).
+        // Consume Q here so the compiler's vmcnt waits for these loads land before the tile
+        // loop, not inside it (where they would also wait for the tile loads in flight).
 #pragma unroll
         for (int j = 0; j < kKSteps; ++j) asm volatile("" ::"v"(qop[j]));
     }
 
-    // ---- per-lane DMA offsets (constant across tiles) and LDS destinations
-    uint32_t voff[C::NPW];
-    uint32_t ldsu[C::NPW];   // unit offset inside a stage, or the dummy sink
+    // ---- this wave's load units of a tile: unit u covers tile bytes [1024 u, 1024 u + 1024);
+    // lane l takes 16-B chunk P = 64 u + l of row r = P / 72, which goes to LDS byte 16 P + 16 r.
+    // Nine units cover exactly eight rows, so the lane part of the LDS offset depends only on
+    // u mod 9 (st9[v]); each wave loads NPW consecutive units, a whole number of 8-row groups.
+    const uint32_t lane16 = (uint32_t)lane * 16u;
+    int st9[9];
 #pragma unroll
-    for (int k = 0; k < C::NPW; ++k) {
-        const int u = rbl + C::RB * k;
-        if (u < C::UNITS) {
-            const int P = u * 64 + lane;
-            const int r = P / kChunksPerRow, pc = P % kChunksPerRow;
-            const int c = pc ^ (r & 7);
-            voff[k] = (uint32_t)(r * kRowBytes + c * 16);
-            ldsu[k] = (uint32_t)(u * 1024);
-        } else {
-            voff[k] = 0x7FFFFFF0u;   // beyond any num_records: loads zeros, touches no memory
-            ldsu[k] = 0xFFFFFFFFu;
-        }
+    for (int v = 0; v < 9; ++v) {
+        const int r0 = (64 * v) / kChunksPerRow;          // row of lane 0 within the 8-row group
+        const int bnd = kChunksPerRow * (r0 + 1) - 64 * v; // first lane in row r0 + 1
+        st9[v] = v * 1024 + 16 * r0 + ((lane >= bnd) ? 16 : 0) + (int)lane16;
     }
-    char* const group_stages = smem + gi * C::NSG * C::STAGE_BYTES;
-    const uint32_t stage0_lds = lds_u32(group_stages);
-    const uint32_t dummy_lds = lds_u32(smem + C::DUMMY_OFF);
+    const int unit0 = wg * C::NPW;                           // first unit of this wave
+    char* const group_stages = smem + gi * C::NS * C::LDS_TILE;
     // Block-table reads go through the constant address space so that the (wave-uniform) loads
-    // become scalar loads counted by lgkmcnt; a vector load here would make the compiler wait
-    // for vmcnt(0), i.e. for every tile DMA in flight.
+    // become scalar loads.
     const __attribute__((address_space(4))) int32_t* bt_row =
         (const __attribute__((address_space(4))) int32_t*)(a.block_table + (size_t)b * a.bt_stride);
     bool bad_page = false;
 
-    auto issue_tile = [&](int itn) {
+    i32x4 rbuf[C::NR][C::NPW];
+    auto load_tile = [&](int itn, auto buf_idx) {
+        constexpr int B = decltype(buf_idx)::value;
         const int k = itn * C::NG + gi;
         if (itn >= n_it || k >= n_tiles) return;
         const int t0 = tok_begin + k * C::TT;
@@ -367,91 +348,109 @@ __global__ void __launch_bounds__(C::THREADS) split_kernel(FwdArgs a)
             bad_page = true;
             valid = 0;
         }
-        const uint64_t base = (uint64_t)(a.cache + ((long long)(valid ? page : 0) * kPage + (t0 % kPage)) * kDk);
-        i32x4 rs;
-        rs[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)base);
-        rs[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32));
-        rs[2] = __builtin_amdgcn_readfirstlane(valid * kRowBytes);
-        rs[3] = 0x00020000;
-        const uint32_t sbase = stage0_lds + (uint32_t)((itn % C::NSG) * C::STAGE_BYTES);
+        const uint16_t* base = a.cache + ((long long)(valid ? page : 0) * kPage + (t0 % kPage)) * kDk;
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, valid * kRowBytes, 0x00020000);
 #pragma unroll
-        for (int u = 0; u < C::NPW; ++u) {
-            const uint32_t dst = (ldsu[u] == 0xFFFFFFFFu) ? dummy_lds : sbase + ldsu[u];
-            dma16(rs, voff[u], __builtin_amdgcn_readfirstlane(dst));
-        }
+        for (int kk = 0; kk < C::NPW; ++kk)
+            rbuf[B][kk] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)lane16, (unit0 + kk) * 1024, kNonTemporal);
     };
-    // tiles of this group still in flight after tile `itn` (each is NPW DMAs of this wave)
-    auto pending_after = [&](int itn) {
-        const int last_issued = min(itn + C::NSG - 2, n_it - 1);
-        int n = 0;
-        for (int t = itn + 1; t <= last_issued; ++t)
-            if (t * C::NG + gi < n_tiles) ++n;
-        return n * C::NPW;
+    auto store_tile = [&](int itn, auto buf_idx) {
+        constexpr int B = decltype(buf_idx)::value;
+        const int k = itn * C::NG + gi;
+        if (itn >= n_it || k >= n_tiles) return;
+        char* stg = group_stages + (itn % C::NS) * C::LDS_TILE + (unit0 / 9) * (8 * kLdsRow);
+#pragma unroll
+        for (int kk = 0; kk < C::NPW; ++kk)
+            *reinterpret_cast<i32x4*>(stg + st9[kk % 9] + (kk / 9) * (8 * kLdsRow)) = rbuf[B][kk];
     };
 
-    // ---- online softmax state: row lr; acc holds O^T[16 dt + 4 lg + i][row lr]
-    f32x4 acc[kDTiles];
+    // ---- online softmax state: row lr; acc[t] holds O^T[16 (dt0 + t) + 4 lg + i][row lr]
+    f32x4 acc[C::DTW];
 #pragma unroll
-    for (int dt = 0; dt < kDTiles; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < C::DTW; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -__builtin_inff();
     float l_run = 0.f;   // lane-partial sum over this lane's tokens
 
-    // K-operand LDS addresses: row = 16 st + lr, chunk (4j + lg) ^ (row & 7)
-    const int ksw = lr & 7;   // (16 st + lr) & 7 == lr & 7
-    const int kb_even = lr * kRowBytes + 16 * (lg ^ (ksw & 3)) + 64 * (ksw >> 2);
-    const int kb_odd = lr * kRowBytes + 16 * (lg ^ (ksw & 3)) - 64 * (ksw >> 2);
-    // V^T tr-read addresses: lane (group lg, i = lr) reads row t = 4 lg + (lr >> 2) (+16 st),
-    // dims 16 dt + 4 (lr & 3) .. +3, i.e. chunk 2 dt + ((lr & 3) >> 1), byte 8 ((lr & 3) & 1)
-    const int vt = 4 * lg + (lr >> 2);
-    const int vsw = vt & 7;
-    const int vq = lr & 3;
-    int vbase[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-        vbase[m] = vt * kRowBytes + 16 * ((vq >> 1) ^ (vsw & 1)) + 8 * (vq & 1) + 32 * ((m ^ (vsw >> 1)) - m);
+    // K-operand LDS address: row 16 st + lr, bytes 64 j + 16 lg (chunk 4j + lg)
+    const int kbase = lr * kLdsRow + 16 * lg;
+    // V^T tr-read address: lane (group lg, i = lr) reads row 4 lg + (lr >> 2) (+16 st), dims
+    // 16 dt + 4 (lr & 3) .. +3
+    const int vbase = (4 * lg + (lr >> 2)) * kLdsRow + 8 * (lr & 3);
 
-    // ---- prologue
-#pragma unroll
-    for (int s = 0; s < C::NSG - 1; ++s) issue_tile(s);
-
-    for (int itn = 0; itn < n_it; ++itn) {
-        wait_vmcnt_le(pending_after(itn));
-        if constexpr (C::RB > 1) __syncthreads();
-        issue_tile(itn + C::NSG - 1);
-        const int k = itn * C::NG + gi;
-        if (k >= n_tiles) continue;
+    // Softmax statistics are rescaled lazily: the running max m_run only moves when a tile's
+    // max exceeds it by more than kLazyRescale (log2 units), so exp2(s - m_run) <= 2^kLazyRescale
+    // and most tiles skip the accumulator rescale; LSE = m_run + log2(l) stays exact.
+    constexpr float kLazyRescale = 8.f;
+    auto kread = [&](const char* p) { return *reinterpret_cast<const bf16x8*>(p); };
+    auto vread = [&](const char* p) {
+        return __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)lds_i16x4(p));
+    };
+    auto compute_tile = [&](int itn, int k) {
         const int t0 = tok_begin + k * C::TT;
-        const char* stg = group_stages + (itn % C::NSG) * C::STAGE_BYTES;
+        const char* stg = group_stages + (itn % C::NS) * C::LDS_TILE;
 
-        // scores S^T[token][row] for each 16-token sub-tile
+        // scores S^T[token][row]: the NST independent 16-token chains are interleaved and their
+        // K operands read KD k-steps ahead (about six MFMAs of cover for the LDS latency)
+        constexpr int KD = C::NST == 1 ? 6 : 3;
         f32x4 s[C::NST];
+        bf16x8 kop[KD + 1][C::NST];
 #pragma unroll
         for (int st = 0; st < C::NST; ++st) {
-            f32x4 c = {0.f, 0.f, 0.f, 0.f};
-            const char* kb = stg + st * 16 * kRowBytes;
+            s[st] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int j = 0; j < kKSteps; ++j) {
-                const bf16x8 kop = *reinterpret_cast<const bf16x8*>(kb + ((j & 1) ? kb_odd : kb_even) + 64 * j);
-                c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[j], c, 0, 0, 0);
-            }
-            s[st] = c;
+            for (int j = 0; j < KD; ++j) kop[j][st] = kread(stg + st * 16 * kLdsRow + kbase + 64 * j);
         }
-        // scale into the log2 domain, mask invisible tokens, tile max per row
+#pragma unroll
+        for (int j = 0; j < kKSteps; ++j) {
+            if (j + KD < kKSteps) {
+#pragma unroll
+                for (int st = 0; st < C::NST; ++st)
+                    kop[(j + KD) % (KD + 1)][st] = kread(stg + st * 16 * kLdsRow + kbase + 64 * (j + KD));
+            }
+#pragma unroll
+            for (int st = 0; st < C::NST; ++st)
+                s[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[j % (KD + 1)][st], qop[j], s[st], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // first V^T operands of the value contraction do not depend on P: start them now
+        constexpr int VD = C::NST == 1 ? 6 : 3;   // d-tiles of look-ahead
+        const char* vt0 = stg + vbase + 32 * dt0;
+        i16x4 vlo[VD + 1], vhi[VD + 1];
+#pragma unroll
+        for (int d = 0; d < VD; ++d) {
+            vlo[d] = vread(vt0 + 32 * d);
+            if constexpr (C::NST >= 2) vhi[d] = vread(vt0 + 16 * kLdsRow + 32 * d);
+        }
+        // scale into the log2 domain, mask invisible tokens (only in a tile that crosses n_vis)
+#pragma unroll
+        for (int st = 0; st < C::NST; ++st) s[st] *= a.scale_log2;
+        if (t0 + C::TT > n_vis) {
+#pragma unroll
+            for (int st = 0; st < C::NST; ++st)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (t0 + 16 * st + 4 * lg + i >= n_vis) s[st][i] = -__builtin_inff();
+        }
         float tmax = -__builtin_inff();
 #pragma unroll
         for (int st = 0; st < C::NST; ++st)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int tok = t0 + 16 * st + 4 * lg + i;
-                const float v = (tok < n_vis) ? s[st][i] * a.scale_log2 : -__builtin_inff();
-                s[st][i] = v;
-                tmax = fmaxf(tmax, v);
-            }
+            tmax = fmaxf(tmax, fmaxf(fmaxf(s[st][0], s[st][1]), fmaxf(s[st][2], s[st][3])));
         tmax = wave_max_groups(tmax);
-        const float m_new = fmaxf(m_run, tmax);
-        const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        m_run = m_new;
+        if (__builtin_amdgcn_ballot_w64(tmax > m_run + kLazyRescale) != 0) {
+            const float m_new = fmaxf(m_run, tmax);
+            const float alpha = (m_new == -__builtin_inff()) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+            // one accumulator tile at a time (the fences keep the scheduler from staging all 128
+            // accumulators in temporaries at once)
+#pragma unroll
+            for (int dt = 0; dt < C::DTW; ++dt) {
+                acc[dt] *= alpha;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        const float m_use = (m_run == -__builtin_inff()) ? 0.f : m_run;
         float psum = 0.f;
         float p[C::NST][4];
 #pragma unroll
@@ -461,91 +460,128 @@ __global__ void __launch_bounds__(C::THREADS) split_kernel(FwdArgs a)
                 p[st][i] = __builtin_amdgcn_exp2f(s[st][i] - m_use);
                 psum += p[st][i];
             }
-        l_run = l_run * alpha + psum;
-#pragma unroll
-        for (int dt = 0; dt < kDTiles; ++dt) acc[dt] *= alpha;
+        l_run += psum;
 
-        if constexpr (C::TT == 32) {
-            bf16x8 pop;
+        // O^T[d][row] += V^T[d][token] P^T[token][row]; V^T comes straight from the K rows in
+        // LDS through transposing reads, two d-tiles ahead of their MFMA
+        if constexpr (C::NST >= 2) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                pop[i] = (__bf16)p[0][i];
-                pop[4 + i] = (__bf16)p[1][i];
-            }
+            for (int h = 0; h < C::NST / 2; ++h) {   // 32-token k-steps
+                bf16x8 pop;
 #pragma unroll
-            for (int dt = 0; dt < kDTiles; ++dt) {
-                const char* v0 = stg + vbase[dt & 3] + 32 * dt;
-                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)lds_i16x4(v0));
-                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (MLA_LDS i16x4*)lds_i16x4(v0 + 16 * kRowBytes));
-                bf16x8 vop;
-                vop = __builtin_shufflevector(__builtin_bit_cast(bf16x4, lo), __builtin_bit_cast(bf16x4, hi),
-                                              0, 1, 2, 3, 4, 5, 6, 7);
-                acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop, acc[dt], 0, 0, 0);
+                for (int i = 0; i < 4; ++i) {
+                    pop[i] = (__bf16)p[2 * h][i];
+                    pop[4 + i] = (__bf16)p[2 * h + 1][i];
+                }
+                const char* vh = vt0 + 32 * h * kLdsRow;
+                if (h > 0) {
+#pragma unroll
+                    for (int d = 0; d < VD; ++d) {
+                        vlo[d] = vread(vh + 32 * d);
+                        vhi[d] = vread(vh + 16 * kLdsRow + 32 * d);
+                    }
+                }
+#pragma unroll
+                for (int dt = 0; dt < C::DTW; ++dt) {
+                    if (dt + VD < C::DTW) {
+                        vlo[(dt + VD) % (VD + 1)] = vread(vh + 32 * (dt + VD));
+                        vhi[(dt + VD) % (VD + 1)] = vread(vh + 16 * kLdsRow + 32 * (dt + VD));
+                    }
+                    const bf16x8 vop = __builtin_shufflevector(__builtin_bit_cast(bf16x4, vlo[dt % (VD + 1)]),
+                                                               __builtin_bit_cast(bf16x4, vhi[dt % (VD + 1)]),
+                                                               0, 1, 2, 3, 4, 5, 6, 7);
+                    acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop, acc[dt], 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
         } else {
             bf16x4 pop;
 #pragma unroll
             for (int i = 0; i < 4; ++i) pop[i] = (__bf16)p[0][i];
 #pragma unroll
-            for (int dt = 0; dt < kDTiles; ++dt) {
-                const char* v0 = stg + vbase[dt & 3] + 32 * dt;
-                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)lds_i16x4(v0));
-                acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, lo), pop, acc[dt],
-                                                                   0, 0, 0);
+            for (int dt = 0; dt < C::DTW; ++dt) {
+                if (dt + VD < C::DTW) vlo[(dt + VD) % (VD + 1)] = vread(vt0 + 32 * (dt + VD));
+                acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, vlo[dt % (VD + 1)]),
+                                                                   pop, acc[dt], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
+    };
+
+    // ---- pipeline: tile itn+1 waits in registers while tile itn is computed from LDS; then it
+    // is stored to LDS and the registers take tile itn+1+NR.
+    auto step = [&](int itn, auto next_buf) {
+        if (itn >= n_it) return;
+        const int k = itn * C::NG + gi;
+        if (k < n_tiles) compute_tile(itn, k);
+        store_tile(itn + 1, next_buf);
+        load_tile(itn + 1 + C::NR, next_buf);
+        if constexpr (C::GW > 1) __syncthreads();
+    };
+    load_tile(0, Idx<0>{});
+    if constexpr (C::NR == 2) load_tile(1, Idx<1>{});
+    store_tile(0, Idx<0>{});
+    load_tile(C::NR, Idx<0>{});
+    if constexpr (C::GW > 1) __syncthreads();
+    if constexpr (C::NR == 2) {
+        for (int itn = 0; itn < n_it; itn += 2) {
+            step(itn, Idx<1>{});
+            step(itn + 1, Idx<0>{});
+        }
+    } else {
+        for (int itn = 0; itn < n_it; ++itn) step(itn, Idx<0>{});
     }
-    wait_vmcnt_le(0);
     l_run = wave_sum_groups(l_run);
 
-    // ---- epilogue: merge the NG wave groups of each row block, write the item's partials
+    // ---- epilogue: merge the NG wave groups of each (row block, segment), write the partials
     const int out_row = row0 + lr;   // row within the sequence (of a.rows)
     if constexpr (C::NG == 1) {
         const float inv = (l_run > 0.f) ? 1.f / l_run : 0.f;
-        float* orow = o_part + (size_t)out_row * kDv;
+        float* orow = o_part + (size_t)out_row * kDv + 16 * dt0;
 #pragma unroll
-        for (int dt = 0; dt < kDTiles; ++dt)
+        for (int dt = 0; dt < C::DTW; ++dt)
             *reinterpret_cast<f32x4*>(orow + 16 * dt + 4 * lg) = acc[dt] * inv;
-        if (lg == 0)
+        if (lg == 0 && dsi == 0)
             lse_part[out_row] = bad_page ? __builtin_nanf("")
                                          : (l_run > 0.f ? (m_run + __builtin_amdgcn_logf(l_run)) * kLn2
                                                         : -__builtin_inff());
     } else {
+        constexpr int SEG = kDv / C::DS;                                 // value dims per wave
         __syncthreads();   // every wave is done with the stages
         float* ml = reinterpret_cast<float*>(smem);                       // [NW][2][16]
-        float* accs = reinterpret_cast<float*>(smem + C::NW * 2 * 16 * 4);  // [NW][16][512]
+        float* accs = reinterpret_cast<float*>(smem + C::NW * 2 * 16 * 4);  // [NW][16][SEG]
         if (lg == 0) {
             ml[(wave * 2 + 0) * 16 + lr] = m_run;
             ml[(wave * 2 + 1) * 16 + lr] = bad_page ? __builtin_nanf("") : l_run;
         }
-        float* my = accs + (size_t)wave * 16 * kDv + lr * kDv;
+        float* my = accs + (size_t)wave * 16 * SEG + lr * SEG;
 #pragma unroll
-        for (int dt = 0; dt < kDTiles; ++dt) *reinterpret_cast<f32x4*>(my + 16 * dt + 4 * lg) = acc[dt];
+        for (int dt = 0; dt < C::DTW; ++dt) *reinterpret_cast<f32x4*>(my + 16 * dt + 4 * lg) = acc[dt];
         __syncthreads();
-        // RB row blocks x 16 rows x 512 dims, all threads
-        for (int e = tid; e < C::RB * 16 * (kDv / 4); e += C::THREADS) {
-            const int d4 = e % (kDv / 4);
-            const int r = (e / (kDv / 4)) % 16;
-            const int rbi = e / (16 * (kDv / 4));
+        // GW waves' worth of (row block, segment) outputs: 16 rows x SEG dims each, all threads
+        for (int e = tid; e < C::GW * 16 * (SEG / 4); e += C::THREADS) {
+            const int d4 = e % (SEG / 4);
+            const int r = (e / (SEG / 4)) % 16;
+            const int w0 = e / (16 * (SEG / 4));                          // wave index within a group
             float M = -__builtin_inff();
-            for (int g = 0; g < C::NG; ++g) M = fmaxf(M, ml[((g * C::RB + rbi) * 2) * 16 + r]);
+            for (int g = 0; g < C::NG; ++g) M = fmaxf(M, ml[((g * C::GW + w0) * 2) * 16 + r]);
             const float Mu = (M == -__builtin_inff()) ? 0.f : M;
             float Lsum = 0.f;
             f32x4 o = {0.f, 0.f, 0.f, 0.f};
             bool nan = false;
             for (int g = 0; g < C::NG; ++g) {
-                const int w = g * C::RB + rbi;
+                const int w = g * C::GW + w0;
                 const float lw = ml[(w * 2 + 1) * 16 + r];
                 nan |= (lw != lw);
                 const float sc = __builtin_amdgcn_exp2f(ml[(w * 2) * 16 + r] - Mu);
                 Lsum += sc * lw;
-                o += sc * *reinterpret_cast<const f32x4*>(accs + ((size_t)w * 16 + r) * kDv + 4 * d4);
+                o += sc * *reinterpret_cast<const f32x4*>(accs + ((size_t)w * 16 + r) * SEG + 4 * d4);
             }
             const float inv = (Lsum > 0.f) ? 1.f / Lsum : 0.f;
+            const int rbi = w0 / C::DS, seg = w0 % C::DS;
             const int grow = (blockIdx.y * C::RB + rbi) * 16 + r;
-            *reinterpret_cast<f32x4*>(o_part + (size_t)grow * kDv + 4 * d4) = o * inv;
-            if (d4 == 0)
+            *reinterpret_cast<f32x4*>(o_part + (size_t)grow * kDv + seg * SEG + 4 * d4) = o * inv;
+            if (d4 == 0 && seg == 0)
                 lse_part[grow] = nan ? __builtin_nanf("")
                                      : (Lsum > 0.f ? (M + __builtin_amdgcn_logf(Lsum)) * kLn2 : -__builtin_inff());
         }
@@ -558,21 +594,20 @@ __global__ void __launch_bounds__(C::THREADS) split_kernel(FwdArgs a)
 // write O as bf16 (round to nearest even) and LSE as fp32.  NaN partials propagate; a row
 // with no key gets O = 0, LSE = -inf.
 // =============================================================================================
-constexpr int kCombineThreads = 256;   // 2 rows x 128 threads x 4 dims
+constexpr int kCombineThreads = 128;   // one (sequence, row) per workgroup, 4 dims per thread
+constexpr int kCombineChunk = 512;     // split weights staged in LDS per pass
 
 __global__ void __launch_bounds__(kCombineThreads) combine_kernel(FwdArgs a)
 {
     const WsLayout lay = ws_layout(a.batch, a.rows, a.capacity);
     const int32_t* header = reinterpret_cast<const int32_t*>(a.ws + lay.header);
-    const int gr = blockIdx.x * 2 + (threadIdx.x >> 7);      // global row = b * rows + r
-    if (gr >= a.batch * a.rows) return;
-    const int t = threadIdx.x & 127;
+    const int gr = blockIdx.x;                 // global row = b * rows + r
+    const int t = threadIdx.x;
     const int b = gr / a.rows;
+    const int r = gr % a.rows;
     const bool shape_ok = header[kHMagic] == kPlanMagic && header[kHBatch] == a.batch &&
                           header[kHSq] == a.s_q && header[kHHeads] == a.heads &&
                           header[kHCapacity] == a.capacity;
-    uint16_t* orow = a.out + (size_t)gr * kDv + 4 * t;
-    const float qnan = __builtin_nanf("");
     bool poison = !shape_ok;
     int s0 = 0, s1 = 0;
     if (shape_ok) {
@@ -583,29 +618,71 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(FwdArgs a)
         s0 = bs[b];
         s1 = bs[b + 1];
     }
-    const int r = gr % a.rows;
     const float* lse_part = reinterpret_cast<const float*>(a.ws + lay.lse_part);
     const float* o_part = reinterpret_cast<const float*>(a.ws + lay.o_part);
+
+    __shared__ float w[kCombineChunk];
+    __shared__ float red_m[kCombineThreads / 64];
+    __shared__ int red_nan[kCombineThreads / 64];
+
+    // pass 1: M = max_s LSE_s (NaN anywhere poisons the row)
     float M = -__builtin_inff();
-    for (int s = s0; s < s1 && !poison; ++s) {
+    int nan = 0;
+    for (int s = s0 + t; s < s1; s += kCombineThreads) {
         const float v = lse_part[(size_t)s * a.rows + r];
-        if (v != v) poison = true;
+        nan |= (v != v);
         M = fmaxf(M, v);
     }
+    for (int o = 32; o > 0; o >>= 1) {
+        M = fmaxf(M, __shfl_xor(M, o));
+        nan |= __shfl_xor(nan, o);
+    }
+    if ((t & 63) == 0) {
+        red_m[t >> 6] = M;
+        red_nan[t >> 6] = nan;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kCombineThreads / 64; ++i) {
+        M = fmaxf(M, red_m[i]);
+        nan |= red_nan[i];
+    }
+    poison |= (nan != 0);
+
+    // pass 2: weights exp(LSE_s - M) through LDS, then the weighted sum of the partial rows
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    float W = 0.f;
+    if (!poison && M != -__builtin_inff()) {
+        for (int c0 = s0; c0 < s1; c0 += kCombineChunk) {
+            const int n = min(kCombineChunk, s1 - c0);
+            __syncthreads();
+            for (int i = t; i < n; i += kCombineThreads) w[i] = expf(lse_part[(size_t)(c0 + i) * a.rows + r] - M);
+            __syncthreads();
+            const float* op = o_part + ((size_t)c0 * a.rows + r) * kDv + 4 * t;
+            const size_t stride = (size_t)a.rows * kDv;
+            int i = 0;
+            for (; i + 4 <= n; i += 4) {
+                const f32x4 v0 = *reinterpret_cast<const f32x4*>(op + (i + 0) * stride);
+                const f32x4 v1 = *reinterpret_cast<const f32x4*>(op + (i + 1) * stride);
+                const f32x4 v2 = *reinterpret_cast<const f32x4*>(op + (i + 2) * stride);
+                const f32x4 v3 = *reinterpret_cast<const f32x4*>(op + (i + 3) * stride);
+                o += w[i] * v0 + w[i + 1] * v1 + w[i + 2] * v2 + w[i + 3] * v3;
+                W += (w[i] + w[i + 1]) + (w[i + 2] + w[i + 3]);
+            }
+            for (; i < n; ++i) {
+                o += w[i] * *reinterpret_cast<const f32x4*>(op + i * stride);
+                W += w[i];
+            }
+        }
+    }
     float lse_out;
     if (poison) {
+        const float qnan = __builtin_nanf("");
         o = f32x4{qnan, qnan, qnan, qnan};
         lse_out = qnan;
     } else if (M == -__builtin_inff()) {
         lse_out = -__builtin_inff();
     } else {
-        float W = 0.f;
-        for (int s = s0; s < s1; ++s) {
-            const float w = expf(lse_part[(size_t)s * a.rows + r] - M);
-            W += w;
-            o += w * *reinterpret_cast<const f32x4*>(o_part + ((size_t)s * a.rows + r) * kDv + 4 * t);
-        }
         o *= 1.f / W;
         lse_out = M + logf(W);
     }
@@ -614,7 +691,7 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(FwdArgs a)
     ob.y = f32_to_bf16_rne(o[1]);
     ob.z = f32_to_bf16_rne(o[2]);
     ob.w = f32_to_bf16_rne(o[3]);
-    *reinterpret_cast<ushort4*>(orow) = ob;
+    *reinterpret_cast<ushort4*>(a.out + (size_t)gr * kDv + 4 * t) = ob;
     if (t == 0) a.lse[gr] = lse_out;
 }
 
