@@ -23,9 +23,9 @@ using namespace mla;
 using CfgR16 = SplitCfg<4, 1, 1, 16, 1, 1>;    // 4 independent waves, one 18 KiB tile each
 using CfgR32 = SplitCfg<4, 2, 1, 32, 2, 1>;    // 2 groups x 2 waves, 2 x 36 KiB stages per group
 using CfgR64 = SplitCfg<4, 4, 1, 32, 2, 1>;    // 1 group of 4 waves, 2 x 36 KiB stages
-using CfgR128 = SplitCfg<8, 8, 1, 64, 2, 1>;   // 1 group of 8 waves x 72 KiB tiles (R = 256: 2 row groups)
+using CfgWide = WideCfg<2>;                    // 128 / 256 rows: row groups of 64 rows, 4 waves each
 
-enum CfgId { kR16 = 0, kR32, kR64, kR128, kNumCfg };
+enum CfgId { kR16 = 0, kR32, kR64, kWide, kNumCfg };
 
 struct LaunchGeom {
     CfgId cfg;
@@ -41,8 +41,8 @@ bool geom_for(int s_q, int heads, LaunchGeom* g)
     case 16: *g = {kR16, 1, CfgR16::THREADS, CfgR16::LDS_BYTES}; return true;
     case 32: *g = {kR32, 1, CfgR32::THREADS, CfgR32::LDS_BYTES}; return true;
     case 64: *g = {kR64, 1, CfgR64::THREADS, CfgR64::LDS_BYTES}; return true;
-    case 128: *g = {kR128, 1, CfgR128::THREADS, CfgR128::LDS_BYTES}; return true;
-    case 256: *g = {kR128, 2, CfgR128::THREADS, CfgR128::LDS_BYTES}; return true;
+    case 128: *g = {kWide, 2, CfgWide::THREADS, CfgWide::LDS_BYTES}; return true;
+    case 256: *g = {kWide, 4, CfgWide::THREADS, CfgWide::LDS_BYTES}; return true;
     default: return false;
     }
 }
@@ -53,7 +53,7 @@ const void* split_fn(CfgId c)
     case kR16: return reinterpret_cast<const void*>(&split_kernel<CfgR16>);
     case kR32: return reinterpret_cast<const void*>(&split_kernel<CfgR32>);
     case kR64: return reinterpret_cast<const void*>(&split_kernel<CfgR64>);
-    default: return reinterpret_cast<const void*>(&split_kernel<CfgR128>);
+    default: return reinterpret_cast<const void*>(&split_wide_kernel<CfgWide>);
     }
 }
 
@@ -93,9 +93,9 @@ int device_info(const DeviceInfo** out)
         } else {
             d.num_cu = prop.multiProcessorCount;
             static const int threads[kNumCfg] = {CfgR16::THREADS, CfgR32::THREADS, CfgR64::THREADS,
-                                                 CfgR128::THREADS};
+                                                 CfgWide::THREADS};
             static const int lds[kNumCfg] = {CfgR16::LDS_BYTES, CfgR32::LDS_BYTES, CfgR64::LDS_BYTES,
-                                             CfgR128::LDS_BYTES};
+                                             CfgWide::LDS_BYTES};
             for (int c = 0; c < kNumCfg; ++c) {
                 const void* fn = split_fn(static_cast<CfgId>(c));
                 int occ = 0;
@@ -212,6 +212,7 @@ int prepare_fwd(const void* q, const void* kv_cache, const int32_t* block_table,
     a->capacity = cap;
     a->scale_log2 = softmax_scale * kLog2e;
     a->causal = causal;
+    a->row_groups = g->row_groups;
     return MLA_OK;
 }
 
@@ -222,7 +223,12 @@ int launch_split(const FwdArgs& a, const LaunchGeom& g, hipStream_t s)
     case kR16: hipLaunchKernelGGL(split_kernel<CfgR16>, grid, dim3(g.threads), g.lds_bytes, s, a); break;
     case kR32: hipLaunchKernelGGL(split_kernel<CfgR32>, grid, dim3(g.threads), g.lds_bytes, s, a); break;
     case kR64: hipLaunchKernelGGL(split_kernel<CfgR64>, grid, dim3(g.threads), g.lds_bytes, s, a); break;
-    default: hipLaunchKernelGGL(split_kernel<CfgR128>, grid, dim3(g.threads), g.lds_bytes, s, a); break;
+    default: {
+        // the row groups of an item get ids 8 apart within blocks of 8 * row_groups ids
+        const int blocks = ((a.capacity + 7) / 8) * 8 * g.row_groups;
+        hipLaunchKernelGGL(split_wide_kernel<CfgWide>, dim3(blocks), dim3(g.threads), g.lds_bytes, s, a);
+        break;
+    }
     }
     return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }

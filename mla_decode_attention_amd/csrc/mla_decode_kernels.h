@@ -27,7 +27,7 @@ constexpr int kDv = 512;
 constexpr int kPage = 64;
 constexpr int kRowBytes = kDk * 2;          // 1152
 constexpr int kChunksPerRow = kRowBytes / 16;  // 72 chunks of 16 B
-constexpr int kLdsRow = kRowBytes + 16;        // LDS row stride: 1168 B = 73 chunks (odd), see below
+constexpr int kLdsRow = kRowBytes + 32;        // LDS row stride: 1184 B = 74 chunks, see below
 constexpr int kKSteps = kDk / 32;           // 18 score MFMA k-steps of 32
 constexpr int kDTiles = kDv / 16;           // 32 output tiles of 16 dims
 constexpr int kPlanMagic = 0x4D4C4131;      // "MLA1"
@@ -169,9 +169,10 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(const int32_t* __res
 // resource of a tile ends at the sequence's last valid row, so rows past L_b load as zeros and
 // never reach the value contraction (0 * NaN would poison it).
 //
-// LDS tile layout: row r of a tile starts at r * 1168 B (16 B of padding per 1152-B row).  An
-// odd number of 16-B chunks per row puts the 16 rows that one K-operand read touches, and the
-// 4 rows of each transposed V read, on distinct bank groups.
+// LDS tile layout: row r of a tile starts at r * 1184 B (32 B of padding per 1152-B row).  With
+// 74 16-B chunks per row (2 x odd), the 32 lanes a K-operand read serves together -- 16 rows x
+// two 16-B chunks -- land on 32 distinct 16-B bank groups of a 512-B bank line (measured: 222
+// B/clk/CU for this pattern vs 122 with 16 B of padding and 62 with none).
 // =============================================================================================
 template <int NW_, int RB_, int DS_, int TT_, int NS_, int NR_>
 struct SplitCfg {
@@ -219,6 +220,7 @@ struct FwdArgs {
     int batch, s_q, heads, rows, capacity;
     float scale_log2;   // softmax_scale * log2(e)
     int causal;
+    int row_groups;     // workgroups per work item (wide form)
 };
 
 __device__ inline const MLA_LDS i16x4* lds_i16x4(const void* p)
@@ -253,6 +255,32 @@ __device__ inline uint16_t f32_to_bf16_rne(float f)
     u += 0x7fffu + ((u >> 16) & 1u);
     return (uint16_t)(u >> 16);
 }
+
+// A 64-entry window of one sequence's block table, one entry per lane of a VGPR: page ids are
+// then read with v_readlane (a few cycles) instead of a scalar load per tile, whose latency
+// would stall the next tile's loads.  The window moves (one vector load) every 64 pages.
+struct PageWindow {
+    const int32_t* row;   // block-table row of the sequence
+    int len;              // entries in the row (bt_stride)
+    int base;             // first entry held (wave-uniform), -1 = none
+    int val;              // lane i: row[base + i]
+
+    __device__ inline void init(const int32_t* r, int n)
+    {
+        row = r;
+        len = n;
+        base = -1;
+        val = 0;
+    }
+    __device__ inline int page(int idx, int lane)
+    {
+        if (base < 0 || idx < base || idx >= base + 64) {
+            base = idx;
+            val = (idx + lane < len) ? row[idx + lane] : -1;
+        }
+        return __builtin_amdgcn_readlane(val, idx - base);
+    }
+};
 
 template <int B>
 struct Idx {
@@ -317,7 +345,7 @@ __global__ void __launch_bounds__(C::THREADS) split_kernel(FwdArgs a)
     }
 
     // ---- this wave's load units of a tile: unit u covers tile bytes [1024 u, 1024 u + 1024);
-    // lane l takes 16-B chunk P = 64 u + l of row r = P / 72, which goes to LDS byte 16 P + 16 r.
+    // lane l takes 16-B chunk P = 64 u + l of row r = P / 72, which goes to LDS byte 16 P + 32 r.
     // Nine units cover exactly eight rows, so the lane part of the LDS offset depends only on
     // u mod 9 (st9[v]); each wave loads NPW consecutive units, a whole number of 8-row groups.
     const uint32_t lane16 = (uint32_t)lane * 16u;
@@ -326,14 +354,12 @@ __global__ void __launch_bounds__(C::THREADS) split_kernel(FwdArgs a)
     for (int v = 0; v < 9; ++v) {
         const int r0 = (64 * v) / kChunksPerRow;          // row of lane 0 within the 8-row group
         const int bnd = kChunksPerRow * (r0 + 1) - 64 * v; // first lane in row r0 + 1
-        st9[v] = v * 1024 + 16 * r0 + ((lane >= bnd) ? 16 : 0) + (int)lane16;
+        st9[v] = v * 1024 + (kLdsRow - kRowBytes) * (r0 + (lane >= bnd ? 1 : 0)) + (int)lane16;
     }
     const int unit0 = wg * C::NPW;                           // first unit of this wave
     char* const group_stages = smem + gi * C::NS * C::LDS_TILE;
-    // Block-table reads go through the constant address space so that the (wave-uniform) loads
-    // become scalar loads.
-    const __attribute__((address_space(4))) int32_t* bt_row =
-        (const __attribute__((address_space(4))) int32_t*)(a.block_table + (size_t)b * a.bt_stride);
+    PageWindow pw;
+    pw.init(a.block_table + (size_t)b * a.bt_stride, a.bt_stride);
     bool bad_page = false;
 
     i32x4 rbuf[C::NR][C::NPW];
@@ -342,7 +368,7 @@ __global__ void __launch_bounds__(C::THREADS) split_kernel(FwdArgs a)
         const int k = itn * C::NG + gi;
         if (itn >= n_it || k >= n_tiles) return;
         const int t0 = tok_begin + k * C::TT;
-        const int page = bt_row[t0 / kPage];
+        const int page = pw.page(t0 / kPage, lane);
         int valid = min(C::TT, L - t0);
         if (page < 0 || (long long)page >= a.num_pages) {
             bad_page = true;
@@ -390,14 +416,19 @@ __global__ void __launch_bounds__(C::THREADS) split_kernel(FwdArgs a)
         const int t0 = tok_begin + k * C::TT;
         const char* stg = group_stages + (itn % C::NS) * C::LDS_TILE;
 
-        // scores S^T[token][row]: the NST independent 16-token chains are interleaved and their
-        // K operands read KD k-steps ahead (about six MFMAs of cover for the LDS latency)
+        // scores S^T[token][row]: a dependent MFMA chain issues only every ~50 cycles, so each
+        // 16-token block accumulates NCH independent partial sums over alternating k-steps
+        // (NST * NCH = 4 chains in flight) that are added at the end; K operands are read KD
+        // k-steps ahead
         constexpr int KD = C::NST == 1 ? 6 : 3;
+        constexpr int NCH = C::NST >= 4 ? 1 : 4 / C::NST;
         f32x4 s[C::NST];
+        f32x4 sp[C::NST][NCH];
         bf16x8 kop[KD + 1][C::NST];
 #pragma unroll
         for (int st = 0; st < C::NST; ++st) {
-            s[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) sp[st][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int j = 0; j < KD; ++j) kop[j][st] = kread(stg + st * 16 * kLdsRow + kbase + 64 * j);
         }
@@ -410,8 +441,15 @@ __global__ void __launch_bounds__(C::THREADS) split_kernel(FwdArgs a)
             }
 #pragma unroll
             for (int st = 0; st < C::NST; ++st)
-                s[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[j % (KD + 1)][st], qop[j], s[st], 0, 0, 0);
+                sp[st][j % NCH] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[j % (KD + 1)][st], qop[j], sp[st][j % NCH], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int st = 0; st < C::NST; ++st) {
+            s[st] = sp[st][0];
+#pragma unroll
+            for (int c = 1; c < NCH; ++c) s[st] += sp[st][c];
         }
         // first V^T operands of the value contraction do not depend on P: start them now
         constexpr int VD = C::NST == 1 ? 6 : 3;   // d-tiles of look-ahead
@@ -585,6 +623,357 @@ __global__ void __launch_bounds__(C::THREADS) split_kernel(FwdArgs a)
                 lse_part[grow] = nan ? __builtin_nanf("")
                                      : (Lsum > 0.f ? (M + __builtin_amdgcn_logf(Lsum)) * kLn2 : -__builtin_inff());
         }
+    }
+}
+
+// =============================================================================================
+// Split kernel, wide form (128 or 256 query rows per sequence: all heads on one GPU).
+//
+// A work item is taken by `row_groups` workgroups of 64 query rows each.  Their ids are 8 apart
+// (id = 8 * row_group + item % 8 within a block of 8 * row_groups ids), so with round-robin
+// dispatch over the 8 XCDs they run together on one XCD and the second read of every KV tile
+// is served by that XCD's L2.
+//
+// Inside a workgroup the four waves split the two contractions differently (the pages' split
+// of the output into segments computed by different warp groups, here by waves):
+//   score:  wave w owns query rows 16w..16w+15 of the group (Q^T in registers), computes
+//           S^T = K Q^T for them, keeps their online-softmax statistics and writes P^T (bf16)
+//           to LDS;
+//   value:  wave w owns value dims 128w..128w+127 for all 64 rows, O^T += V^T P^T, reading the
+//           V^T operand once per 16 dims and reusing it across the four 16-row blocks.
+// One barrier per 32-token tile separates the two; P^T is double-buffered.  Tiles stream
+// HBM -> VGPR -> LDS as in the row-block form (three stages, two tiles in flight per wave).
+// =============================================================================================
+template <int NR_>
+struct WideCfg {
+    static constexpr int NW = 4;              // waves per workgroup (one per SIMD)
+    static constexpr int RW = 64;             // query rows per workgroup
+    static constexpr int TT = 32;             // tokens per tile
+    static constexpr int NS = 3;              // LDS stages
+    static constexpr int NR = NR_;            // tiles in flight in registers per wave
+    static constexpr int SEG = kDv / NW;      // value dims per wave
+    static constexpr int DTW = SEG / 16;      // 16-dim output tiles per wave
+    static constexpr int LDS_TILE = TT * kLdsRow;
+    static constexpr int UNITS = TT * kRowBytes / 1024;     // 1-KiB load units per tile
+    static constexpr int NPW = UNITS / NW;                  // per wave
+    static constexpr int P_BYTES = RW * TT * 2;             // bf16 P^T of one tile
+    static constexpr int OFF_P = NS * LDS_TILE;
+    static constexpr int OFF_ALPHA = OFF_P + 2 * P_BYTES;   // fp32 [2][RW] rescale factors
+    static constexpr int OFF_FLAG = OFF_ALPHA + 2 * RW * 4; // int [2][NW] rescale flags
+    static constexpr int OFF_ML = OFF_FLAG + 2 * NW * 4;    // fp32 [2][RW] final m, l
+    static constexpr int LDS_BYTES = OFF_ML + 2 * RW * 4;
+    static constexpr int THREADS = NW * 64;
+    static_assert(NPW * NW == UNITS && NPW % 9 == 0, "each wave loads whole 8-row groups");
+    static_assert(NR == 1 || NR == 2, "one or two tiles in flight per wave");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+};
+
+template <class C>
+__global__ void __launch_bounds__(C::THREADS) split_wide_kernel(FwdArgs a)
+{
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lr = lane & 15;
+    const int lg = lane >> 4;
+
+    const int G = a.row_groups;
+    const int x = blockIdx.x;
+    const int item = (x / (8 * G)) * 8 + x % 8;
+    const int rg = (x / 8) % G;
+
+    const WsLayout lay = ws_layout(a.batch, a.rows, a.capacity);
+    const int32_t* header = reinterpret_cast<const int32_t*>(a.ws + lay.header);
+    if (header[kHMagic] != kPlanMagic || header[kHBatch] != a.batch || header[kHSq] != a.s_q ||
+        header[kHHeads] != a.heads || header[kHCapacity] != a.capacity)
+        return;  // the combine kernel reports the mismatch
+    if (item >= header[kHItems]) return;
+    const i32x4 it = reinterpret_cast<const i32x4*>(a.ws + lay.items)[item];
+    const int b = it[0];
+    const int L = a.seqlens[b];
+    const int32_t plan_L = reinterpret_cast<const int32_t*>(a.ws + lay.seqlens)[b];
+    float* lse_part = reinterpret_cast<float*>(a.ws + lay.lse_part) + (size_t)item * a.rows;
+    float* o_part = reinterpret_cast<float*>(a.ws + lay.o_part) + (size_t)item * a.rows * kDv;
+
+    const int row_base = rg * C::RW;                  // first row of this group
+    const int srow = row_base + 16 * wave + lr;       // this lane's score row
+    const int qi = row_base / a.heads;                // the group's query token (heads % 64 == 0)
+    const bool bad_seq = (L != plan_L) || L < 0 || (long long)L > (long long)kPage * a.bt_stride;
+    if (bad_seq) {
+        if (tid < C::RW) lse_part[row_base + tid] = __builtin_nanf("");
+        return;
+    }
+    const int n_vis = a.causal ? min(max(L - a.s_q + 1 + qi, 0), L) : L;
+    const int tok_begin = it[1] * kPage;
+    const int tok_end = min(it[2] * kPage, L);
+    const int n_tiles = (tok_end - tok_begin + C::TT - 1) / C::TT;
+
+    bf16x8 qop[kKSteps];
+    {
+        const uint16_t* qrow = a.q + ((size_t)(b * a.s_q + srow / a.heads) * a.heads + srow % a.heads) * kDk;
+#pragma unroll
+        for (int j = 0; j < kKSteps; ++j)
+            qop[j] = *reinterpret_cast<const bf16x8*>(qrow + 32 * j + 8 * lg);
+#pragma unroll
+        for (int j = 0; j < kKSteps; ++j) asm volatile("" ::"v"(qop[j]));
+    }
+
+    const uint32_t lane16 = (uint32_t)lane * 16u;
+    int st9[9];
+#pragma unroll
+    for (int v = 0; v < 9; ++v) {
+        const int r0 = (64 * v) / kChunksPerRow;
+        const int bnd = kChunksPerRow * (r0 + 1) - 64 * v;
+        st9[v] = v * 1024 + (kLdsRow - kRowBytes) * (r0 + (lane >= bnd ? 1 : 0)) + (int)lane16;
+    }
+    const int unit0 = wave * C::NPW;
+    PageWindow pw;
+    pw.init(a.block_table + (size_t)b * a.bt_stride, a.bt_stride);
+    bool bad_page = false;
+
+    i32x4 rbuf[C::NR][C::NPW];
+    auto load_tile = [&](int t, auto buf_idx) {
+        constexpr int B = decltype(buf_idx)::value;
+        if (t >= n_tiles) return;
+        const int t0 = tok_begin + t * C::TT;
+        const int page = pw.page(t0 / kPage, lane);
+        int valid = min(C::TT, L - t0);
+        if (page < 0 || (long long)page >= a.num_pages) {
+            bad_page = true;
+            valid = 0;
+        }
+        const uint16_t* base = a.cache + ((long long)(valid ? page : 0) * kPage + (t0 % kPage)) * kDk;
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, valid * kRowBytes, 0x00020000);
+#pragma unroll
+        for (int kk = 0; kk < C::NPW; ++kk)
+            rbuf[B][kk] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)lane16, (unit0 + kk) * 1024, kNonTemporal);
+    };
+    auto store_tile = [&](int t, auto buf_idx) {
+        constexpr int B = decltype(buf_idx)::value;
+        if (t >= n_tiles) return;
+        char* stg = smem + (t % C::NS) * C::LDS_TILE + (unit0 / 9) * (8 * kLdsRow);
+#pragma unroll
+        for (int kk = 0; kk < C::NPW; ++kk)
+            *reinterpret_cast<i32x4*>(stg + st9[kk % 9] + (kk / 9) * (8 * kLdsRow)) = rbuf[B][kk];
+    };
+
+    // score side: statistics of row srow (lane-partial l)
+    float m_run = -__builtin_inff();
+    float l_run = 0.f;
+    constexpr float kLazyRescale = 8.f;
+    // value side: acc[dt][rb] holds O^T[SEG w + 16 dt + 4 lg + i][row_base + 16 rb + lr]
+    f32x4 acc[C::DTW][4];
+#pragma unroll
+    for (int dt = 0; dt < C::DTW; ++dt)
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) acc[dt][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int kbase = lr * kLdsRow + 16 * lg;
+    const int vbase = (4 * lg + (lr >> 2)) * kLdsRow + 8 * (lr & 3) + 32 * (wave * C::DTW);
+    char* const pbuf0 = smem + C::OFF_P;
+    float* const alpha_s = reinterpret_cast<float*>(smem + C::OFF_ALPHA);
+    int* const flag_s = reinterpret_cast<int*>(smem + C::OFF_FLAG);
+    auto kread = [&](const char* p) { return *reinterpret_cast<const bf16x8*>(p); };
+    auto vread = [&](const char* p) {
+        return __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)lds_i16x4(p));
+    };
+
+    // score(t): S^T for the wave's 16 rows over tile t; softmax(t): online softmax and P^T (bf16)
+    // to LDS.  P^T slot 8 lg + i of row r holds token 4 lg + i (i < 4) or 16 + 4 lg + (i - 4):
+    // the lane's own accumulator values, so each lane writes one 16-B chunk.
+    // value(t): O^T[dims of this wave][64 rows] += V^T P^T over tile t.
+    // Score and value MFMAs of consecutive tiles are independent, so after each barrier the wave
+    // runs score(t) interleaved with value(t - 1): one stream's LDS reads are in flight while the
+    // other's MFMAs issue.
+    constexpr int KD = 3;   // K-operand look-ahead (k-steps of two MFMAs)
+    constexpr int VD = 2;   // V-operand look-ahead (16-dim tiles of four MFMAs)
+    f32x4 s[2];
+    auto softmax = [&](int t) {
+        const int t0 = tok_begin + t * C::TT;
+#pragma unroll
+        for (int st = 0; st < 2; ++st) s[st] *= a.scale_log2;
+        if (t0 + C::TT > n_vis) {
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (t0 + 16 * st + 4 * lg + i >= n_vis) s[st][i] = -__builtin_inff();
+        }
+        float tmax = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                           fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+        tmax = wave_max_groups(tmax);
+        const int par = t & 1;
+        int rescaled = 0;
+        if (__builtin_amdgcn_ballot_w64(tmax > m_run + kLazyRescale) != 0) {
+            const float m_new = fmaxf(m_run, tmax);
+            const float alpha = (m_new == -__builtin_inff()) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+            if (lg == 0) alpha_s[par * C::RW + 16 * wave + lr] = alpha;
+            rescaled = 1;
+        }
+        if (lane == 0) flag_s[par * C::NW + wave] = rescaled;
+        const float m_use = (m_run == -__builtin_inff()) ? 0.f : m_run;
+        float psum = 0.f;
+        bf16x8 pk;
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float pv = __builtin_amdgcn_exp2f(s[st][i] - m_use);
+                psum += pv;
+                pk[4 * st + i] = (__bf16)pv;
+            }
+        l_run += psum;
+        *reinterpret_cast<bf16x8*>(pbuf0 + par * C::P_BYTES + (16 * wave + lr) * (C::TT * 2) + 16 * lg) = pk;
+    };
+    // rows of a block that took a new max in tile t: rescale their accumulators
+    auto rescale_acc = [&](int t) {
+        const int par = t & 1;
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+            if (flag_s[par * C::NW + rb] != 0) {
+                const float al = alpha_s[par * C::RW + 16 * rb + lr];
+#pragma unroll
+                for (int dt = 0; dt < C::DTW; ++dt) {
+                    acc[dt][rb] *= al;
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        }
+    };
+    // DO_S: run score(ts); DO_V: run value(tv); both: interleaved
+    auto fused = [&](int ts, int tv, auto do_s, auto do_v) {
+        constexpr bool DO_S = decltype(do_s)::value != 0;
+        constexpr bool DO_V = decltype(do_v)::value != 0;
+        const char* sst = smem + (ts % C::NS) * C::LDS_TILE;
+        const char* vst = smem + (tv % C::NS) * C::LDS_TILE;
+        bf16x8 kop[KD + 1][2];
+        bf16x8 pop[4];
+        i16x4 vlo[VD + 1], vhi[VD + 1];
+        if constexpr (DO_V) rescale_acc(tv);
+        // two 16-token blocks x two k-parities = four independent score chains (a dependent
+        // MFMA chain issues only every ~50 cycles)
+        f32x4 sp[2][2];
+        if constexpr (DO_S) {
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                sp[st][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+                sp[st][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < KD; ++j) kop[j][st] = kread(sst + st * 16 * kLdsRow + kbase + 64 * j);
+            }
+        }
+        const char* vt0 = vst + vbase;
+        if constexpr (DO_V) {
+            const char* pb = pbuf0 + (tv & 1) * C::P_BYTES;
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) pop[rb] = kread(pb + (16 * rb + lr) * (C::TT * 2) + 16 * lg);
+#pragma unroll
+            for (int d = 0; d < VD; ++d) {
+                vlo[d] = vread(vt0 + 32 * d);
+                vhi[d] = vread(vt0 + 16 * kLdsRow + 32 * d);
+            }
+        }
+        // 18 score steps (2 MFMAs each) with the 8 value tiles (4 MFMAs each) slotted in after
+        // odd steps
+#pragma unroll
+        for (int j = 0; j < kKSteps; ++j) {
+            if constexpr (DO_S) {
+                if (j + KD < kKSteps) {
+#pragma unroll
+                    for (int st = 0; st < 2; ++st)
+                        kop[(j + KD) % (KD + 1)][st] = kread(sst + st * 16 * kLdsRow + kbase + 64 * (j + KD));
+                }
+#pragma unroll
+                for (int st = 0; st < 2; ++st)
+                    sp[st][j & 1] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[j % (KD + 1)][st], qop[j], sp[st][j & 1], 0, 0, 0);
+            }
+            if constexpr (DO_V) {
+                if ((j & 1) && (j >> 1) < C::DTW) {
+                    const int dt = j >> 1;
+                    if (dt + VD < C::DTW) {
+                        vlo[(dt + VD) % (VD + 1)] = vread(vt0 + 32 * (dt + VD));
+                        vhi[(dt + VD) % (VD + 1)] = vread(vt0 + 16 * kLdsRow + 32 * (dt + VD));
+                    }
+                    const bf16x8 vop = __builtin_shufflevector(__builtin_bit_cast(bf16x4, vlo[dt % (VD + 1)]),
+                                                               __builtin_bit_cast(bf16x4, vhi[dt % (VD + 1)]),
+                                                               0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+                    for (int rb = 0; rb < 4; ++rb)
+                        acc[dt][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[rb], acc[dt][rb], 0, 0, 0);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (DO_S) {
+#pragma unroll
+            for (int st = 0; st < 2; ++st) s[st] = sp[st][0] + sp[st][1];
+        }
+    };
+
+    // ---- pipeline.  At the top of iteration t, stages t%3 and (t+1)%3 hold tiles t and t+1
+    // and the registers hold tiles t+2 (buffer t&1) and t+3.  Iteration t scores tile t and
+    // finishes the value contraction of tile t-1 (P^T(t-1) became visible at the previous
+    // barrier), then publishes P^T(t) at its barrier, after which the stage of tile t-1 is free
+    // and receives tile t+2 (visible at the next barrier, two iterations before it is scored).
+    auto step = [&](int t, auto buf) {
+        if (t >= n_tiles) return;
+        if (t == 0)
+            fused(t, t, Idx<1>{}, Idx<0>{});
+        else
+            fused(t, t - 1, Idx<1>{}, Idx<1>{});
+        softmax(t);
+        __syncthreads();
+        store_tile(t + 2, buf);
+        load_tile(t + 2 + C::NR, buf);
+    };
+    load_tile(0, Idx<0>{});
+    if constexpr (C::NR == 2) {
+        load_tile(1, Idx<1>{});
+        store_tile(0, Idx<0>{});
+        load_tile(2, Idx<0>{});
+        store_tile(1, Idx<1>{});
+        load_tile(3, Idx<1>{});
+    } else {
+        store_tile(0, Idx<0>{});
+        load_tile(1, Idx<0>{});
+        store_tile(1, Idx<0>{});
+        load_tile(2, Idx<0>{});
+    }
+    __syncthreads();
+    if constexpr (C::NR == 2) {
+        for (int t = 0; t < n_tiles; t += 2) {
+            step(t, Idx<0>{});
+            step(t + 1, Idx<1>{});
+        }
+    } else {
+        for (int t = 0; t < n_tiles; ++t) step(t, Idx<0>{});
+    }
+    if (n_tiles > 0) fused(n_tiles - 1, n_tiles - 1, Idx<0>{}, Idx<1>{});   // value of the last tile
+    l_run = wave_sum_groups(l_run);
+
+    // ---- epilogue: share final (m, l) of every row, normalise and write the item's partials
+    float* ml_s = reinterpret_cast<float*>(smem + C::OFF_ML);
+    if (lg == 0) {
+        ml_s[16 * wave + lr] = m_run;
+        ml_s[C::RW + 16 * wave + lr] = l_run;
+        lse_part[srow] = bad_page ? __builtin_nanf("")
+                                  : (l_run > 0.f ? (m_run + __builtin_amdgcn_logf(l_run)) * kLn2
+                                                 : -__builtin_inff());
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+        const float l = ml_s[C::RW + 16 * rb + lr];
+        const float inv = (l > 0.f) ? 1.f / l : 0.f;
+        float* orow = o_part + (size_t)(row_base + 16 * rb + lr) * kDv + C::SEG * wave;
+#pragma unroll
+        for (int dt = 0; dt < C::DTW; ++dt)
+            *reinterpret_cast<f32x4*>(orow + 16 * dt + 4 * lg) = acc[dt][rb] * inv;
     }
 }
 
