@@ -634,36 +634,40 @@ __global__ void __launch_bounds__(C::THREADS) split_kernel(FwdArgs a)
 // dispatch over the 8 XCDs they run together on one XCD and the second read of every KV tile
 // is served by that XCD's L2.
 //
-// Inside a workgroup the four waves split the two contractions differently (the pages' split
-// of the output into segments computed by different warp groups, here by waves):
-//   score:  wave w owns query rows 16w..16w+15 of the group (Q^T in registers), computes
+// Eight waves, two per SIMD, in two roles (the pages' split of the work between warp groups):
+//   score waves 0-3: wave w owns query rows 16w..16w+15 (Q^T in registers), computes
 //           S^T = K Q^T for them, keeps their online-softmax statistics and writes P^T (bf16)
-//           to LDS;
-//   value:  wave w owns value dims 128w..128w+127 for all 64 rows, O^T += V^T P^T, reading the
-//           V^T operand once per 16 dims and reusing it across the four 16-row blocks.
-// One barrier per 32-token tile separates the two; P^T is double-buffered.  Tiles stream
-// HBM -> VGPR -> LDS as in the row-block form (three stages, two tiles in flight per wave).
+//           and the rescale factors to LDS;
+//   value waves 4-7: wave 4+w owns value dims 128w..128w+127 of all 64 rows and accumulates
+//           O^T += V^T P^T, reading each V^T operand once for the four 16-row blocks.
+// With two waves per SIMD one wave's MFMAs run while the other waits or does vector work.
+// Both roles stream the KV tiles HBM -> VGPR -> LDS (each wave a fixed share of every tile).
+// Step t: score waves score tile t+1 and run the softmax of tile t; value waves accumulate
+// tile t-1; one barrier per step.  LDS holds four tile stages: t-1 (value), t (waiting for its
+// value step), t+1 (score), t+2 (landing).
 // =============================================================================================
 template <int NR_>
 struct WideCfg {
-    static constexpr int NW = 4;              // waves per workgroup (one per SIMD)
+    static constexpr int NW = 8;              // waves per workgroup: 4 score + 4 value
     static constexpr int RW = 64;             // query rows per workgroup
     static constexpr int TT = 32;             // tokens per tile
-    static constexpr int NS = 3;              // LDS stages
+    static constexpr int NS = 4;              // LDS stages
     static constexpr int NR = NR_;            // tiles in flight in registers per wave
-    static constexpr int SEG = kDv / NW;      // value dims per wave
-    static constexpr int DTW = SEG / 16;      // 16-dim output tiles per wave
+    static constexpr int SEG = kDv / 4;       // value dims per value wave
+    static constexpr int DTW = SEG / 16;      // 16-dim output tiles per value wave
     static constexpr int LDS_TILE = TT * kLdsRow;
-    static constexpr int UNITS = TT * kRowBytes / 1024;     // 1-KiB load units per tile
-    static constexpr int NPW = UNITS / NW;                  // per wave
-    static constexpr int P_BYTES = RW * TT * 2;             // bf16 P^T of one tile
+    static constexpr int UNITS = TT * kRowBytes / 1024;     // 1-KiB load units per tile (36)
+    static constexpr int US = 5;                            // units of an 8-row group a score wave moves
+    static constexpr int UV = 9 - US;                       // ... and its value-wave partner
+    static constexpr int P_ROW = TT * 2;                    // bytes of one P^T row (bf16)
+    static constexpr int P_BYTES = RW * P_ROW;              // P^T of one tile
     static constexpr int OFF_P = NS * LDS_TILE;
     static constexpr int OFF_ALPHA = OFF_P + 2 * P_BYTES;   // fp32 [2][RW] rescale factors
-    static constexpr int OFF_FLAG = OFF_ALPHA + 2 * RW * 4; // int [2][NW] rescale flags
-    static constexpr int OFF_ML = OFF_FLAG + 2 * NW * 4;    // fp32 [2][RW] final m, l
+    static constexpr int OFF_FLAG = OFF_ALPHA + 2 * RW * 4; // int [2][4] rescale flags
+    static constexpr int OFF_ML = OFF_FLAG + 2 * 4 * 4;     // fp32 [2][RW] final m, l
     static constexpr int LDS_BYTES = OFF_ML + 2 * RW * 4;
     static constexpr int THREADS = NW * 64;
-    static_assert(NPW * NW == UNITS && NPW % 9 == 0, "each wave loads whole 8-row groups");
+    static_assert(UNITS == 36, "four 8-row groups of nine 1-KiB units");
     static_assert(NR == 1 || NR == 2, "one or two tiles in flight per wave");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
@@ -675,6 +679,8 @@ __global__ void __launch_bounds__(C::THREADS) split_wide_kernel(FwdArgs a)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int w4 = wave & 3;                 // row block (score) / dim segment (value) / 8-row group
+    const bool is_score = wave < 4;
     const int lr = lane & 15;
     const int lg = lane >> 4;
 
@@ -697,7 +703,7 @@ __global__ void __launch_bounds__(C::THREADS) split_wide_kernel(FwdArgs a)
     float* o_part = reinterpret_cast<float*>(a.ws + lay.o_part) + (size_t)item * a.rows * kDv;
 
     const int row_base = rg * C::RW;                  // first row of this group
-    const int srow = row_base + 16 * wave + lr;       // this lane's score row
+    const int srow = row_base + 16 * w4 + lr;         // score waves: this lane's row
     const int qi = row_base / a.heads;                // the group's query token (heads % 64 == 0)
     const bool bad_seq = (L != plan_L) || L < 0 || (long long)L > (long long)kPage * a.bt_stride;
     if (bad_seq) {
@@ -709,33 +715,20 @@ __global__ void __launch_bounds__(C::THREADS) split_wide_kernel(FwdArgs a)
     const int tok_end = min(it[2] * kPage, L);
     const int n_tiles = (tok_end - tok_begin + C::TT - 1) / C::TT;
 
-    bf16x8 qop[kKSteps];
-    {
-        const uint16_t* qrow = a.q + ((size_t)(b * a.s_q + srow / a.heads) * a.heads + srow % a.heads) * kDk;
-#pragma unroll
-        for (int j = 0; j < kKSteps; ++j)
-            qop[j] = *reinterpret_cast<const bf16x8*>(qrow + 32 * j + 8 * lg);
-#pragma unroll
-        for (int j = 0; j < kKSteps; ++j) asm volatile("" ::"v"(qop[j]));
-    }
-
+    // ---- tile staging, shared by both roles: the waves w and w + 4 move 8-row group w of every
+    // tile, the score wave units 0 .. US-1 and the value wave units US .. 8 of the group.  Lane l
+    // of unit u takes 16-B chunk 64 u + l of the group, which lands at LDS byte st9(u) of the
+    // group (rows padded to kLdsRow bytes).
     const uint32_t lane16 = (uint32_t)lane * 16u;
-    int st9[9];
-#pragma unroll
-    for (int v = 0; v < 9; ++v) {
+    auto st9 = [&](int v) __attribute__((always_inline)) {   // v is a compile-time constant
         const int r0 = (64 * v) / kChunksPerRow;
         const int bnd = kChunksPerRow * (r0 + 1) - 64 * v;
-        st9[v] = v * 1024 + (kLdsRow - kRowBytes) * (r0 + (lane >= bnd ? 1 : 0)) + (int)lane16;
-    }
-    const int unit0 = wave * C::NPW;
+        return v * 1024 + (kLdsRow - kRowBytes) * (r0 + (lane >= bnd ? 1 : 0)) + (int)lane16;
+    };
     PageWindow pw;
     pw.init(a.block_table + (size_t)b * a.bt_stride, a.bt_stride);
     bool bad_page = false;
-
-    i32x4 rbuf[C::NR][C::NPW];
-    auto load_tile = [&](int t, auto buf_idx) {
-        constexpr int B = decltype(buf_idx)::value;
-        if (t >= n_tiles) return;
+    auto tile_rsrc = [&](int t) __attribute__((always_inline)) {
         const int t0 = tok_begin + t * C::TT;
         const int page = pw.page(t0 / kPage, lane);
         int valid = min(C::TT, L - t0);
@@ -744,157 +737,278 @@ __global__ void __launch_bounds__(C::THREADS) split_wide_kernel(FwdArgs a)
             valid = 0;
         }
         const uint16_t* base = a.cache + ((long long)(valid ? page : 0) * kPage + (t0 % kPage)) * kDk;
-        const __amdgpu_buffer_rsrc_t rs =
-            __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, valid * kRowBytes, 0x00020000);
-#pragma unroll
-        for (int kk = 0; kk < C::NPW; ++kk)
-            rbuf[B][kk] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)lane16, (unit0 + kk) * 1024, kNonTemporal);
+        return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, valid * kRowBytes, 0x00020000);
     };
-    auto store_tile = [&](int t, auto buf_idx) {
-        constexpr int B = decltype(buf_idx)::value;
-        if (t >= n_tiles) return;
-        char* stg = smem + (t % C::NS) * C::LDS_TILE + (unit0 / 9) * (8 * kLdsRow);
-#pragma unroll
-        for (int kk = 0; kk < C::NPW; ++kk)
-            *reinterpret_cast<i32x4*>(stg + st9[kk % 9] + (kk / 9) * (8 * kLdsRow)) = rbuf[B][kk];
+    auto no_rsrc = [&]() __attribute__((always_inline)) {
+        return __builtin_amdgcn_make_buffer_rsrc((void*)a.cache, (short)0, 0, 0x00020000);
     };
-
-    // score side: statistics of row srow (lane-partial l)
-    float m_run = -__builtin_inff();
-    float l_run = 0.f;
-    constexpr float kLazyRescale = 8.f;
-    // value side: acc[dt][rb] holds O^T[SEG w + 16 dt + 4 lg + i][row_base + 16 rb + lr]
-    f32x4 acc[C::DTW][4];
-#pragma unroll
-    for (int dt = 0; dt < C::DTW; ++dt)
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) acc[dt][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // U0: first unit of the group this wave moves; NU: how many
+    auto load_unit = [&](i32x4& dst, __amdgpu_buffer_rsrc_t rs, int u) __attribute__((always_inline)) {
+        dst = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)lane16, (9 * w4 + u) * 1024, kNonTemporal);
+    };
+    auto store_unit = [&](int t, const i32x4& src, int u) __attribute__((always_inline)) {
+        char* stg = smem + (t % C::NS) * C::LDS_TILE + w4 * (8 * kLdsRow);
+        *reinterpret_cast<i32x4*>(stg + st9(u)) = src;
+    };
 
     const int kbase = lr * kLdsRow + 16 * lg;
-    const int vbase = (4 * lg + (lr >> 2)) * kLdsRow + 8 * (lr & 3) + 32 * (wave * C::DTW);
+    const int vbase = (4 * lg + (lr >> 2)) * kLdsRow + 8 * (lr & 3) + 32 * (w4 * C::DTW);
+    // P^T: row r (64 B) keeps its 16-B chunk c at chunk c ^ ((r >> 2) & 3), so the 16 rows of a
+    // block read or written by one instruction spread over all LDS banks
+    const int pchunk = 16 * (lg ^ ((lr >> 2) & 3));
     char* const pbuf0 = smem + C::OFF_P;
     float* const alpha_s = reinterpret_cast<float*>(smem + C::OFF_ALPHA);
     int* const flag_s = reinterpret_cast<int*>(smem + C::OFF_FLAG);
-    auto kread = [&](const char* p) { return *reinterpret_cast<const bf16x8*>(p); };
-    auto vread = [&](const char* p) {
+    float* const ml_s = reinterpret_cast<float*>(smem + C::OFF_ML);
+    auto kread = [&](const char* p) __attribute__((always_inline)) { return *reinterpret_cast<const bf16x8*>(p); };
+    auto vread = [&](const char* p) __attribute__((always_inline)) {
         return __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)lds_i16x4(p));
     };
+    constexpr int NR = C::NR;
 
-    // score(t): S^T for the wave's 16 rows over tile t; softmax(t): online softmax and P^T (bf16)
-    // to LDS.  P^T slot 8 lg + i of row r holds token 4 lg + i (i < 4) or 16 + 4 lg + (i - 4):
-    // the lane's own accumulator values, so each lane writes one 16-B chunk.
-    // value(t): O^T[dims of this wave][64 rows] += V^T P^T over tile t.
-    // Score and value MFMAs of consecutive tiles are independent, so after each barrier the wave
-    // runs score(t) interleaved with value(t - 1): one stream's LDS reads are in flight while the
-    // other's MFMAs issue.
-    constexpr int KD = 3;   // K-operand look-ahead (k-steps of two MFMAs)
-    constexpr int VD = 2;   // V-operand look-ahead (16-dim tiles of four MFMAs)
-    f32x4 s[2];
-    auto softmax = [&](int t) {
-        const int t0 = tok_begin + t * C::TT;
+    // One role's pipeline.  ROLE_STEP(t, buf, full, ...) runs step t; every wave runs the same
+    // steps and barriers.  Before step t: stages hold tiles t-1, t, t+1 (t+1 published), P^T(t-1)
+    // published, rbuf[t & (NR-1)] = tile t+2 (arrived or in flight), the other buffer tile t+3.
+    // Step t: store tile t+2, load tile t+2+NR, role work; barrier.
+    auto run_pipeline = [&](auto nu_tag, auto u0_tag, auto&& prologue_work, auto&& role_step,
+                            auto&& epilogue_work) __attribute__((always_inline)) {
+        constexpr int NU = decltype(nu_tag)::value;
+        constexpr int U0 = decltype(u0_tag)::value;
+        i32x4 rbuf[NR][NU];
+        auto load_all = [&](int t, auto buf) __attribute__((always_inline)) {
+            constexpr int B = decltype(buf)::value;
+            const __amdgpu_buffer_rsrc_t r = tile_rsrc(t);
 #pragma unroll
-        for (int st = 0; st < 2; ++st) s[st] *= a.scale_log2;
-        if (t0 + C::TT > n_vis) {
+            for (int k = 0; k < NU; ++k) load_unit(rbuf[B][k], r, U0 + k);
+        };
+        auto store_all = [&](int t, auto buf) __attribute__((always_inline)) {
+            constexpr int B = decltype(buf)::value;
 #pragma unroll
-            for (int st = 0; st < 2; ++st)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (t0 + 16 * st + 4 * lg + i >= n_vis) s[st][i] = -__builtin_inff();
-        }
-        float tmax = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                           fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-        tmax = wave_max_groups(tmax);
-        const int par = t & 1;
-        int rescaled = 0;
-        if (__builtin_amdgcn_ballot_w64(tmax > m_run + kLazyRescale) != 0) {
-            const float m_new = fmaxf(m_run, tmax);
-            const float alpha = (m_new == -__builtin_inff()) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-            m_run = m_new;
-            l_run *= alpha;
-            if (lg == 0) alpha_s[par * C::RW + 16 * wave + lr] = alpha;
-            rescaled = 1;
-        }
-        if (lane == 0) flag_s[par * C::NW + wave] = rescaled;
-        const float m_use = (m_run == -__builtin_inff()) ? 0.f : m_run;
-        float psum = 0.f;
-        bf16x8 pk;
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float pv = __builtin_amdgcn_exp2f(s[st][i] - m_use);
-                psum += pv;
-                pk[4 * st + i] = (__bf16)pv;
-            }
-        l_run += psum;
-        *reinterpret_cast<bf16x8*>(pbuf0 + par * C::P_BYTES + (16 * wave + lr) * (C::TT * 2) + 16 * lg) = pk;
-    };
-    // rows of a block that took a new max in tile t: rescale their accumulators
-    auto rescale_acc = [&](int t) {
-        const int par = t & 1;
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-            if (flag_s[par * C::NW + rb] != 0) {
-                const float al = alpha_s[par * C::RW + 16 * rb + lr];
-#pragma unroll
-                for (int dt = 0; dt < C::DTW; ++dt) {
-                    acc[dt][rb] *= al;
-                    __builtin_amdgcn_sched_barrier(0);
+            for (int k = 0; k < NU; ++k) store_unit(t, rbuf[B][k], U0 + k);
+        };
+        // staging part of step t, spread over the role's k-steps: store unit k of tile t+2 in
+        // slot 2k, load it again (tile t+2+NR) in slot 2k+1
+        auto stage = [&](int t, auto buf, int slot, bool do_st, bool do_ld,
+                         __amdgpu_buffer_rsrc_t rs) __attribute__((always_inline)) {
+            constexpr int B = decltype(buf)::value;
+            const int k = slot >> 1;
+            if (k < NU) {
+                if ((slot & 1) == 0) {
+                    if (do_st) store_unit(t + 2, rbuf[B][k], U0 + k);
+                } else {
+                    if (do_ld) load_unit(rbuf[B][k], rs, U0 + k);
                 }
             }
+        };
+        if (n_tiles == 0) {   // uniform per workgroup: both roles skip the same barriers
+            epilogue_work();
+            return;
         }
+        if constexpr (NR == 2) {
+            load_all(0, Idx<0>{});
+            if (n_tiles > 1) load_all(1, Idx<1>{});
+            store_all(0, Idx<0>{});
+            if (n_tiles > 2) load_all(2, Idx<0>{});
+            if (n_tiles > 1) store_all(1, Idx<1>{});
+            if (n_tiles > 3) load_all(3, Idx<1>{});
+        } else {
+            load_all(0, Idx<0>{});
+            store_all(0, Idx<0>{});
+            if (n_tiles > 1) {
+                load_all(1, Idx<0>{});
+                store_all(1, Idx<0>{});
+            }
+            if (n_tiles > 2) load_all(2, Idx<0>{});
+        }
+        __syncthreads();
+        prologue_work();
+        auto any_step = [&](int t, auto buf) __attribute__((always_inline)) {
+            const bool do_st = t + 2 < n_tiles, do_ld = t + 2 + NR < n_tiles;
+            const __amdgpu_buffer_rsrc_t rs = do_ld ? tile_rsrc(t + 2 + NR) : no_rsrc();
+            role_step(t, Idx<0>{}, [&](int slot) __attribute__((always_inline)) {
+                stage(t, buf, slot, do_st, do_ld, rs);
+            });
+            __syncthreads();
+        };
+        auto full_step = [&](int t, auto buf) __attribute__((always_inline)) {
+            const __amdgpu_buffer_rsrc_t rs = tile_rsrc(t + 2 + NR);
+            role_step(t, Idx<1>{}, [&](int slot) __attribute__((always_inline)) {
+                stage(t, buf, slot, true, true, rs);
+            });
+            __syncthreads();
+        };
+        any_step(0, Idx<0>{});
+        int t = 1;
+        if constexpr (NR == 2) {
+            for (; t + 3 + NR < n_tiles; t += 2) {   // steps t (odd) and t + 1 have every part
+                full_step(t, Idx<1>{});
+                full_step(t + 1, Idx<0>{});
+            }
+            for (; t < n_tiles; ++t) {
+                if (t & 1)
+                    any_step(t, Idx<1>{});
+                else
+                    any_step(t, Idx<0>{});
+            }
+        } else {
+            for (; t + 2 + NR < n_tiles; ++t) full_step(t, Idx<0>{});
+            for (; t < n_tiles; ++t) any_step(t, Idx<0>{});
+        }
+        epilogue_work();
     };
-    // DO_S: run score(ts); DO_V: run value(tv); both: interleaved
-    auto fused = [&](int ts, int tv, auto do_s, auto do_v) {
-        constexpr bool DO_S = decltype(do_s)::value != 0;
-        constexpr bool DO_V = decltype(do_v)::value != 0;
-        const char* sst = smem + (ts % C::NS) * C::LDS_TILE;
-        const char* vst = smem + (tv % C::NS) * C::LDS_TILE;
-        bf16x8 kop[KD + 1][2];
-        bf16x8 pop[4];
-        i16x4 vlo[VD + 1], vhi[VD + 1];
-        if constexpr (DO_V) rescale_acc(tv);
-        // two 16-token blocks x two k-parities = four independent score chains (a dependent
-        // MFMA chain issues only every ~50 cycles)
-        f32x4 sp[2][2];
-        if constexpr (DO_S) {
+
+    constexpr float kLazyRescale = 8.f;
+    if (is_score) {
+        // ================= score role =================
+        bf16x8 qop[kKSteps];
+        {
+            const uint16_t* qrow = a.q + ((size_t)(b * a.s_q + srow / a.heads) * a.heads + srow % a.heads) * kDk;
 #pragma unroll
-            for (int st = 0; st < 2; ++st) {
-                sp[st][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-                sp[st][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < kKSteps; ++j)
+                qop[j] = *reinterpret_cast<const bf16x8*>(qrow + 32 * j + 8 * lg);
 #pragma unroll
-                for (int j = 0; j < KD; ++j) kop[j][st] = kread(sst + st * 16 * kLdsRow + kbase + 64 * j);
-            }
+            for (int j = 0; j < kKSteps; ++j) asm volatile("" ::"v"(qop[j]));
         }
-        const char* vt0 = vst + vbase;
-        if constexpr (DO_V) {
-            const char* pb = pbuf0 + (tv & 1) * C::P_BYTES;
+        float m_run = -__builtin_inff();
+        float l_run = 0.f;   // lane-partial sum over this lane's tokens
+        f32x4 s[2];          // S^T of the tile awaiting its softmax: token 16 st + 4 lg + i of row srow
+        constexpr int KD = 3;   // K-operand look-ahead (k-steps of two MFMAs)
+        // S^T of tile ts; the staging slots and the softmax pieces of tile tsm run between the
+        // k-steps (softmax pieces read s, the new scores go to sn and replace s at the end)
+        auto score_step = [&](int ts, bool do_s, int tsm, bool do_sm, auto&& slot_fn) __attribute__((always_inline)) {
+            const char* sst = smem + (ts % C::NS) * C::LDS_TILE;
+            bf16x8 kop[KD + 1][2];
+            f32x4 sp[2][2];
+            if (do_s) {
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb) pop[rb] = kread(pb + (16 * rb + lr) * (C::TT * 2) + 16 * lg);
+                for (int st = 0; st < 2; ++st) {
+                    sp[st][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    sp[st][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int d = 0; d < VD; ++d) {
-                vlo[d] = vread(vt0 + 32 * d);
-                vhi[d] = vread(vt0 + 16 * kLdsRow + 32 * d);
+                    for (int j = 0; j < KD; ++j) kop[j][st] = kread(sst + st * 16 * kLdsRow + kbase + 64 * j);
+                }
             }
-        }
-        // 18 score steps (2 MFMAs each) with the 8 value tiles (4 MFMAs each) slotted in after
-        // odd steps
+            float tmax = 0.f;
+            bf16x8 pk;
 #pragma unroll
-        for (int j = 0; j < kKSteps; ++j) {
-            if constexpr (DO_S) {
-                if (j + KD < kKSteps) {
+            for (int j = 0; j < kKSteps; ++j) {
+                if (do_s) {
+                    if (j + KD < kKSteps) {
+#pragma unroll
+                        for (int st = 0; st < 2; ++st)
+                            kop[(j + KD) % (KD + 1)][st] = kread(sst + st * 16 * kLdsRow + kbase + 64 * (j + KD));
+                    }
 #pragma unroll
                     for (int st = 0; st < 2; ++st)
-                        kop[(j + KD) % (KD + 1)][st] = kread(sst + st * 16 * kLdsRow + kbase + 64 * (j + KD));
+                        sp[st][j & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[j % (KD + 1)][st], qop[j],
+                                                                                sp[st][j & 1], 0, 0, 0);
                 }
+                if (do_sm) {
+                    const int par = tsm & 1;
+                    if (j == 1) {   // scale into the log2 domain, mask, lane max
+                        const int t0 = tok_begin + tsm * C::TT;
 #pragma unroll
-                for (int st = 0; st < 2; ++st)
-                    sp[st][j & 1] =
-                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[j % (KD + 1)][st], qop[j], sp[st][j & 1], 0, 0, 0);
+                        for (int st = 0; st < 2; ++st)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const float v = s[st][i] * a.scale_log2;
+                                s[st][i] = (t0 + 16 * st + 4 * lg + i >= n_vis) ? -__builtin_inff() : v;
+                            }
+                        tmax = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+                    }
+                    if (j == 3) tmax = wave_max_groups(tmax);
+                    if (j == 5) {   // lazy max update; alpha and this block's flag go to LDS
+                        const bool resc = __builtin_amdgcn_ballot_w64(tmax > m_run + kLazyRescale) != 0;
+                        const float m_new = resc ? fmaxf(m_run, tmax) : m_run;
+                        const float alpha = (m_new == -__builtin_inff()) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+                        m_run = m_new;
+                        l_run *= alpha;
+                        alpha_s[par * C::RW + 16 * w4 + lr] = alpha;   // the four lanes of a row agree
+                        flag_s[par * 4 + w4] = resc ? 1 : 0;
+                    }
+                    if (j == 7 || j == 9) {   // probabilities of one 16-token block
+                        const int h = (j - 7) / 2;
+                        const float m_use = (m_run == -__builtin_inff()) ? 0.f : m_run;
+                        float psum = 0.f;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float pv = __builtin_amdgcn_exp2f(s[h][i] - m_use);
+                            psum += pv;
+                            pk[4 * h + i] = (__bf16)pv;
+                        }
+                        l_run += psum;
+                    }
+                    if (j == 11)   // P^T slot 8 lg + i holds token 4 lg + i (i < 4) or 16 + 4 lg + (i - 4)
+                        *reinterpret_cast<bf16x8*>(pbuf0 + par * C::P_BYTES + (16 * w4 + lr) * C::P_ROW + pchunk) = pk;
+                }
+                slot_fn(j);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            if constexpr (DO_V) {
-                if ((j & 1) && (j >> 1) < C::DTW) {
-                    const int dt = j >> 1;
+            if (do_s) {
+#pragma unroll
+                for (int st = 0; st < 2; ++st) s[st] = sp[st][0] + sp[st][1];
+            }
+        };
+        run_pipeline(
+            Idx<C::US>{}, Idx<0>{},
+            [&]() __attribute__((always_inline)) {   // s = S^T(0)
+                if (n_tiles > 0) score_step(0, true, 0, false, [](int) {});
+            },
+            [&](int t, auto full, auto&& slot_fn) __attribute__((always_inline)) {
+                constexpr bool F = decltype(full)::value != 0;
+                score_step(t + 1, F || t + 1 < n_tiles, t, true, slot_fn);
+            },
+            [&]() __attribute__((always_inline)) {
+                l_run = wave_sum_groups(l_run);
+                if (lg == 0) {
+                    ml_s[16 * w4 + lr] = m_run;
+                    ml_s[C::RW + 16 * w4 + lr] = l_run;
+                    lse_part[srow] = bad_page ? __builtin_nanf("")
+                                              : (l_run > 0.f ? (m_run + __builtin_amdgcn_logf(l_run)) * kLn2
+                                                             : -__builtin_inff());
+                }
+                __syncthreads();
+            });
+    } else {
+        // ================= value role =================
+        // acc[dt][rb] holds O^T[SEG w4 + 16 dt + 4 lg + i][row_base + 16 rb + lr]
+        f32x4 acc[C::DTW][4];
+#pragma unroll
+        for (int dt = 0; dt < C::DTW; ++dt)
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) acc[dt][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        constexpr int VD = 2;   // V-operand look-ahead (16-dim tiles of four MFMAs)
+        auto value_step = [&](int tv, bool do_v, auto&& slot_fn) __attribute__((always_inline)) {
+            const char* vt0 = smem + (tv % C::NS) * C::LDS_TILE + vbase;
+            bf16x8 pop[4];
+            i16x4 vlo[VD + 1], vhi[VD + 1];
+            if (do_v) {
+                const int par = tv & 1;
+                // rows of a block that took a new max in tile tv: rescale their accumulators
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb) {
+                    if (flag_s[par * 4 + rb] != 0) {
+                        const float al = alpha_s[par * C::RW + 16 * rb + lr];
+#pragma unroll
+                        for (int dt = 0; dt < C::DTW; ++dt) {
+                            acc[dt][rb] *= al;
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                    }
+                }
+                const char* pb = pbuf0 + par * C::P_BYTES;
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb) pop[rb] = kread(pb + (16 * rb + lr) * C::P_ROW + pchunk);
+#pragma unroll
+                for (int d = 0; d < VD; ++d) {
+                    vlo[d] = vread(vt0 + 32 * d);
+                    vhi[d] = vread(vt0 + 16 * kLdsRow + 32 * d);
+                }
+            }
+#pragma unroll
+            for (int dt = 0; dt < C::DTW; ++dt) {
+                if (do_v) {
                     if (dt + VD < C::DTW) {
                         vlo[(dt + VD) % (VD + 1)] = vread(vt0 + 32 * (dt + VD));
                         vhi[(dt + VD) % (VD + 1)] = vread(vt0 + 16 * kLdsRow + 32 * (dt + VD));
@@ -906,74 +1020,32 @@ __global__ void __launch_bounds__(C::THREADS) split_wide_kernel(FwdArgs a)
                     for (int rb = 0; rb < 4; ++rb)
                         acc[dt][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[rb], acc[dt][rb], 0, 0, 0);
                 }
+                slot_fn(dt);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        if constexpr (DO_S) {
+            // the staging slots past the eight d-tiles
 #pragma unroll
-            for (int st = 0; st < 2; ++st) s[st] = sp[st][0] + sp[st][1];
-        }
-    };
-
-    // ---- pipeline.  At the top of iteration t, stages t%3 and (t+1)%3 hold tiles t and t+1
-    // and the registers hold tiles t+2 (buffer t&1) and t+3.  Iteration t scores tile t and
-    // finishes the value contraction of tile t-1 (P^T(t-1) became visible at the previous
-    // barrier), then publishes P^T(t) at its barrier, after which the stage of tile t-1 is free
-    // and receives tile t+2 (visible at the next barrier, two iterations before it is scored).
-    auto step = [&](int t, auto buf) {
-        if (t >= n_tiles) return;
-        if (t == 0)
-            fused(t, t, Idx<1>{}, Idx<0>{});
-        else
-            fused(t, t - 1, Idx<1>{}, Idx<1>{});
-        softmax(t);
-        __syncthreads();
-        store_tile(t + 2, buf);
-        load_tile(t + 2 + C::NR, buf);
-    };
-    load_tile(0, Idx<0>{});
-    if constexpr (C::NR == 2) {
-        load_tile(1, Idx<1>{});
-        store_tile(0, Idx<0>{});
-        load_tile(2, Idx<0>{});
-        store_tile(1, Idx<1>{});
-        load_tile(3, Idx<1>{});
-    } else {
-        store_tile(0, Idx<0>{});
-        load_tile(1, Idx<0>{});
-        store_tile(1, Idx<0>{});
-        load_tile(2, Idx<0>{});
-    }
-    __syncthreads();
-    if constexpr (C::NR == 2) {
-        for (int t = 0; t < n_tiles; t += 2) {
-            step(t, Idx<0>{});
-            step(t + 1, Idx<1>{});
-        }
-    } else {
-        for (int t = 0; t < n_tiles; ++t) step(t, Idx<0>{});
-    }
-    if (n_tiles > 0) fused(n_tiles - 1, n_tiles - 1, Idx<0>{}, Idx<1>{});   // value of the last tile
-    l_run = wave_sum_groups(l_run);
-
-    // ---- epilogue: share final (m, l) of every row, normalise and write the item's partials
-    float* ml_s = reinterpret_cast<float*>(smem + C::OFF_ML);
-    if (lg == 0) {
-        ml_s[16 * wave + lr] = m_run;
-        ml_s[C::RW + 16 * wave + lr] = l_run;
-        lse_part[srow] = bad_page ? __builtin_nanf("")
-                                  : (l_run > 0.f ? (m_run + __builtin_amdgcn_logf(l_run)) * kLn2
-                                                 : -__builtin_inff());
-    }
-    __syncthreads();
+            for (int sl = C::DTW; sl < 2 * C::UV; ++sl) slot_fn(sl);
+        };
+        run_pipeline(
+            Idx<C::UV>{}, Idx<C::US>{}, [&]() __attribute__((always_inline)) {},
+            [&](int t, auto full, auto&& slot_fn) __attribute__((always_inline)) {
+                constexpr bool F = decltype(full)::value != 0;
+                value_step(t - 1, F || t >= 1, slot_fn);
+            },
+            [&]() __attribute__((always_inline)) {
+                if (n_tiles > 0) value_step(n_tiles - 1, true, [](int) {});   // value of the last tile
+                __syncthreads();
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-        const float l = ml_s[C::RW + 16 * rb + lr];
-        const float inv = (l > 0.f) ? 1.f / l : 0.f;
-        float* orow = o_part + (size_t)(row_base + 16 * rb + lr) * kDv + C::SEG * wave;
+                for (int rb = 0; rb < 4; ++rb) {
+                    const float l = ml_s[C::RW + 16 * rb + lr];
+                    const float inv = (l > 0.f) ? 1.f / l : 0.f;
+                    float* orow = o_part + (size_t)(row_base + 16 * rb + lr) * kDv + C::SEG * w4;
 #pragma unroll
-        for (int dt = 0; dt < C::DTW; ++dt)
-            *reinterpret_cast<f32x4*>(orow + 16 * dt + 4 * lg) = acc[dt][rb] * inv;
+                    for (int dt = 0; dt < C::DTW; ++dt)
+                        *reinterpret_cast<f32x4*>(orow + 16 * dt + 4 * lg) = acc[dt][rb] * inv;
+                }
+            });
     }
 }
 
