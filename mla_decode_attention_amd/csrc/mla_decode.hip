@@ -23,7 +23,7 @@ using namespace mla;
 using CfgR16 = SplitCfg<4, 1, 1, 16, 1, 1>;    // 4 independent waves, one 18 KiB tile each
 using CfgR32 = SplitCfg<4, 2, 1, 32, 2, 1>;    // 2 groups x 2 waves, 2 x 36 KiB stages per group
 using CfgR64 = SplitCfg<4, 4, 1, 32, 2, 1>;    // 1 group of 4 waves, 2 x 36 KiB stages
-using CfgWide = WideCfg<1>;                    // 128 / 256 rows: row groups of 64 rows, 4 waves each
+using CfgWide = WideCfg<1, 5>;                 // 128 / 256 rows: row groups of 64 rows, 8 waves each
 
 enum CfgId { kR16 = 0, kR32, kR64, kWide, kNumCfg };
 

@@ -277,6 +277,9 @@ struct PageWindow {
         if (base < 0 || idx < base || idx >= base + 64) {
             base = idx;
             val = (idx + lane < len) ? row[idx + lane] : -1;
+            // wait here for the refill (vmcnt 0 only), so the common path needs no wait on the
+            // tile loads in flight before its readlane
+            __builtin_amdgcn_s_waitcnt(0x0F70);
         }
         return __builtin_amdgcn_readlane(val, idx - base);
     }
@@ -646,7 +649,7 @@ __global__ void __launch_bounds__(C::THREADS) split_kernel(FwdArgs a)
 // tile t-1; one barrier per step.  LDS holds four tile stages: t-1 (value), t (waiting for its
 // value step), t+1 (score), t+2 (landing).
 // =============================================================================================
-template <int NR_>
+template <int NR_, int US_>
 struct WideCfg {
     static constexpr int NW = 8;              // waves per workgroup: 4 score + 4 value
     static constexpr int RW = 64;             // query rows per workgroup
@@ -657,7 +660,7 @@ struct WideCfg {
     static constexpr int DTW = SEG / 16;      // 16-dim output tiles per value wave
     static constexpr int LDS_TILE = TT * kLdsRow;
     static constexpr int UNITS = TT * kRowBytes / 1024;     // 1-KiB load units per tile (36)
-    static constexpr int US = 5;                            // units of an 8-row group a score wave moves
+    static constexpr int US = US_;                          // units of an 8-row group a score wave moves
     static constexpr int UV = 9 - US;                       // ... and its value-wave partner
     static constexpr int P_ROW = TT * 2;                    // bytes of one P^T row (bf16)
     static constexpr int P_BYTES = RW * P_ROW;              // P^T of one tile
@@ -669,6 +672,7 @@ struct WideCfg {
     static constexpr int THREADS = NW * 64;
     static_assert(UNITS == 36, "four 8-row groups of nine 1-KiB units");
     static_assert(NR == 1 || NR == 2, "one or two tiles in flight per wave");
+    static_assert(US >= 1 && US <= 9, "score waves move 1..9 units of their group");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
@@ -774,12 +778,17 @@ __global__ void __launch_bounds__(C::THREADS) split_wide_kernel(FwdArgs a)
                             auto&& epilogue_work) __attribute__((always_inline)) {
         constexpr int NU = decltype(nu_tag)::value;
         constexpr int U0 = decltype(u0_tag)::value;
-        i32x4 rbuf[NR][NU];
+        i32x4 rbuf[NR][NU > 0 ? NU : 1];
+        // Loads are issued on every path (a tile past the end reads zeros through an empty
+        // resource and is never stored), so the number of loads in flight is the same on every
+        // path and each store waits only for its own unit.
         auto load_all = [&](int t, auto buf) __attribute__((always_inline)) {
             constexpr int B = decltype(buf)::value;
-            const __amdgpu_buffer_rsrc_t r = tile_rsrc(t);
+            if constexpr (NU > 0) {
+                const __amdgpu_buffer_rsrc_t r = t < n_tiles ? tile_rsrc(t) : no_rsrc();
 #pragma unroll
-            for (int k = 0; k < NU; ++k) load_unit(rbuf[B][k], r, U0 + k);
+                for (int k = 0; k < NU; ++k) load_unit(rbuf[B][k], r, U0 + k);
+            }
         };
         auto store_all = [&](int t, auto buf) __attribute__((always_inline)) {
             constexpr int B = decltype(buf)::value;
@@ -792,11 +801,12 @@ __global__ void __launch_bounds__(C::THREADS) split_wide_kernel(FwdArgs a)
                          __amdgpu_buffer_rsrc_t rs) __attribute__((always_inline)) {
             constexpr int B = decltype(buf)::value;
             const int k = slot >> 1;
-            if (k < NU) {
+            if (NU > 0 && k < NU) {
                 if ((slot & 1) == 0) {
                     if (do_st) store_unit(t + 2, rbuf[B][k], U0 + k);
                 } else {
-                    if (do_ld) load_unit(rbuf[B][k], rs, U0 + k);
+                    (void)do_ld;   // rs is empty when the tile is past the end
+                    load_unit(rbuf[B][k], rs, U0 + k);
                 }
             }
         };
@@ -806,24 +816,22 @@ __global__ void __launch_bounds__(C::THREADS) split_wide_kernel(FwdArgs a)
         }
         if constexpr (NR == 2) {
             load_all(0, Idx<0>{});
-            if (n_tiles > 1) load_all(1, Idx<1>{});
+            load_all(1, Idx<1>{});
             store_all(0, Idx<0>{});
-            if (n_tiles > 2) load_all(2, Idx<0>{});
+            load_all(2, Idx<0>{});
             if (n_tiles > 1) store_all(1, Idx<1>{});
-            if (n_tiles > 3) load_all(3, Idx<1>{});
+            load_all(3, Idx<1>{});
         } else {
             load_all(0, Idx<0>{});
             store_all(0, Idx<0>{});
-            if (n_tiles > 1) {
-                load_all(1, Idx<0>{});
-                store_all(1, Idx<0>{});
-            }
-            if (n_tiles > 2) load_all(2, Idx<0>{});
+            load_all(1, Idx<0>{});
+            if (n_tiles > 1) store_all(1, Idx<0>{});
+            load_all(2, Idx<0>{});
         }
         __syncthreads();
         prologue_work();
         auto any_step = [&](int t, auto buf) __attribute__((always_inline)) {
-            const bool do_st = t + 2 < n_tiles, do_ld = t + 2 + NR < n_tiles;
+            const bool do_st = t + 2 < n_tiles, do_ld = NU > 0 && t + 2 + NR < n_tiles;
             const __amdgpu_buffer_rsrc_t rs = do_ld ? tile_rsrc(t + 2 + NR) : no_rsrc();
             role_step(t, Idx<0>{}, [&](int slot) __attribute__((always_inline)) {
                 stage(t, buf, slot, do_st, do_ld, rs);
@@ -831,7 +839,7 @@ __global__ void __launch_bounds__(C::THREADS) split_wide_kernel(FwdArgs a)
             __syncthreads();
         };
         auto full_step = [&](int t, auto buf) __attribute__((always_inline)) {
-            const __amdgpu_buffer_rsrc_t rs = tile_rsrc(t + 2 + NR);
+            const __amdgpu_buffer_rsrc_t rs = NU > 0 ? tile_rsrc(t + 2 + NR) : no_rsrc();
             role_step(t, Idx<1>{}, [&](int slot) __attribute__((always_inline)) {
                 stage(t, buf, slot, true, true, rs);
             });
@@ -986,9 +994,10 @@ __global__ void __launch_bounds__(C::THREADS) split_wide_kernel(FwdArgs a)
             if (do_v) {
                 const int par = tv & 1;
                 // rows of a block that took a new max in tile tv: rescale their accumulators
+                const i32x4 flags = *reinterpret_cast<const i32x4*>(flag_s + par * 4);
 #pragma unroll
                 for (int rb = 0; rb < 4; ++rb) {
-                    if (flag_s[par * 4 + rb] != 0) {
+                    if (__builtin_amdgcn_readfirstlane(flags[rb]) != 0) {
                         const float al = alpha_s[par * C::RW + 16 * rb + lr];
 #pragma unroll
                         for (int dt = 0; dt < C::DTW; ++dt) {
