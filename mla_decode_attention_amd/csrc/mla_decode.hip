@@ -16,16 +16,16 @@ namespace {
 using namespace mla;
 
 // Launch configurations by query rows per sequence (s_q * heads).
-// A wave owns one 16-row block (or, with DS > 1, a 512/DS-dim segment of it).  For 16-32 rows,
-// four waves per CU with one 18-36 KiB tile in flight each stream as fast as eight (measured),
-// so the smaller-register eight-wave form is kept for wider row counts only.
+// 16 rows: four independent waves per CU, each streaming its own 16-token tiles (the work per
+// byte is small enough that one wave per SIMD keeps HBM busy).  32 rows and more: the
+// eight-wave score/value form, whose two waves per SIMD overlap MFMA, LDS and vector work.
 //                         waves  row-blocks  segments  tile tokens  LDS stages  register tiles
 using CfgR16 = SplitCfg<4, 1, 1, 16, 1, 1>;    // 4 independent waves, one 18 KiB tile each
-using CfgR32 = SplitCfg<4, 2, 1, 32, 2, 1>;    // 2 groups x 2 waves, 2 x 36 KiB stages per group
-using CfgR64 = SplitCfg<4, 4, 1, 32, 2, 1>;    // 1 group of 4 waves, 2 x 36 KiB stages
-using CfgWide = WideCfg<1, 5>;                 // 128 / 256 rows: row groups of 64 rows, 8 waves each
+//                     register tiles  score-wave load units  16-row blocks
+using CfgW32 = WideCfg<1, 5, 2>;               // 32 rows per workgroup
+using CfgW64 = WideCfg<1, 5, 4>;               // 64 rows per workgroup (row groups of 64 above)
 
-enum CfgId { kR16 = 0, kR32, kR64, kWide, kNumCfg };
+enum CfgId { kR16 = 0, kW32, kW64, kNumCfg };
 
 struct LaunchGeom {
     CfgId cfg;
@@ -39,10 +39,10 @@ bool geom_for(int s_q, int heads, LaunchGeom* g)
     const int rows = s_q * heads;
     switch (rows) {
     case 16: *g = {kR16, 1, CfgR16::THREADS, CfgR16::LDS_BYTES}; return true;
-    case 32: *g = {kR32, 1, CfgR32::THREADS, CfgR32::LDS_BYTES}; return true;
-    case 64: *g = {kR64, 1, CfgR64::THREADS, CfgR64::LDS_BYTES}; return true;
-    case 128: *g = {kWide, 2, CfgWide::THREADS, CfgWide::LDS_BYTES}; return true;
-    case 256: *g = {kWide, 4, CfgWide::THREADS, CfgWide::LDS_BYTES}; return true;
+    case 32: *g = {kW32, 1, CfgW32::THREADS, CfgW32::LDS_BYTES}; return true;
+    case 64: *g = {kW64, 1, CfgW64::THREADS, CfgW64::LDS_BYTES}; return true;
+    case 128: *g = {kW64, 2, CfgW64::THREADS, CfgW64::LDS_BYTES}; return true;
+    case 256: *g = {kW64, 4, CfgW64::THREADS, CfgW64::LDS_BYTES}; return true;
     default: return false;
     }
 }
@@ -51,9 +51,8 @@ const void* split_fn(CfgId c)
 {
     switch (c) {
     case kR16: return reinterpret_cast<const void*>(&split_kernel<CfgR16>);
-    case kR32: return reinterpret_cast<const void*>(&split_kernel<CfgR32>);
-    case kR64: return reinterpret_cast<const void*>(&split_kernel<CfgR64>);
-    default: return reinterpret_cast<const void*>(&split_wide_kernel<CfgWide>);
+    case kW32: return reinterpret_cast<const void*>(&split_wide_kernel<CfgW32>);
+    default: return reinterpret_cast<const void*>(&split_wide_kernel<CfgW64>);
     }
 }
 
@@ -92,10 +91,8 @@ int device_info(const DeviceInfo** out)
             d.status = MLA_ERR_NO_DEVICE;   // the code objects are built for gfx950 only
         } else {
             d.num_cu = prop.multiProcessorCount;
-            static const int threads[kNumCfg] = {CfgR16::THREADS, CfgR32::THREADS, CfgR64::THREADS,
-                                                 CfgWide::THREADS};
-            static const int lds[kNumCfg] = {CfgR16::LDS_BYTES, CfgR32::LDS_BYTES, CfgR64::LDS_BYTES,
-                                             CfgWide::LDS_BYTES};
+            static const int threads[kNumCfg] = {CfgR16::THREADS, CfgW32::THREADS, CfgW64::THREADS};
+            static const int lds[kNumCfg] = {CfgR16::LDS_BYTES, CfgW32::LDS_BYTES, CfgW64::LDS_BYTES};
             for (int c = 0; c < kNumCfg; ++c) {
                 const void* fn = split_fn(static_cast<CfgId>(c));
                 int occ = 0;
@@ -218,17 +215,14 @@ int prepare_fwd(const void* q, const void* kv_cache, const int32_t* block_table,
 
 int launch_split(const FwdArgs& a, const LaunchGeom& g, hipStream_t s)
 {
-    const dim3 grid(a.capacity, g.row_groups);
+    // wide forms: the row groups of an item get ids 8 apart within blocks of 8 * row_groups ids
+    const int blocks = ((a.capacity + 7) / 8) * 8 * g.row_groups;
     switch (g.cfg) {
-    case kR16: hipLaunchKernelGGL(split_kernel<CfgR16>, grid, dim3(g.threads), g.lds_bytes, s, a); break;
-    case kR32: hipLaunchKernelGGL(split_kernel<CfgR32>, grid, dim3(g.threads), g.lds_bytes, s, a); break;
-    case kR64: hipLaunchKernelGGL(split_kernel<CfgR64>, grid, dim3(g.threads), g.lds_bytes, s, a); break;
-    default: {
-        // the row groups of an item get ids 8 apart within blocks of 8 * row_groups ids
-        const int blocks = ((a.capacity + 7) / 8) * 8 * g.row_groups;
-        hipLaunchKernelGGL(split_wide_kernel<CfgWide>, dim3(blocks), dim3(g.threads), g.lds_bytes, s, a);
+    case kR16:
+        hipLaunchKernelGGL(split_kernel<CfgR16>, dim3(a.capacity, g.row_groups), dim3(g.threads), g.lds_bytes, s, a);
         break;
-    }
+    case kW32: hipLaunchKernelGGL(split_wide_kernel<CfgW32>, dim3(blocks), dim3(g.threads), g.lds_bytes, s, a); break;
+    default: hipLaunchKernelGGL(split_wide_kernel<CfgW64>, dim3(blocks), dim3(g.threads), g.lds_bytes, s, a); break;
     }
     return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }

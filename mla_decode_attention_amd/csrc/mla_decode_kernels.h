@@ -649,10 +649,11 @@ __global__ void __launch_bounds__(C::THREADS) split_kernel(FwdArgs a)
 // tile t-1; one barrier per step.  LDS holds four tile stages: t-1 (value), t (waiting for its
 // value step), t+1 (score), t+2 (landing).
 // =============================================================================================
-template <int NR_, int US_>
+template <int NR_, int US_, int NRB_>
 struct WideCfg {
     static constexpr int NW = 8;              // waves per workgroup: 4 score + 4 value
-    static constexpr int RW = 64;             // query rows per workgroup
+    static constexpr int NRB = NRB_;          // 16-row blocks per workgroup (2 or 4)
+    static constexpr int RW = 16 * NRB;       // query rows per workgroup
     static constexpr int TT = 32;             // tokens per tile
     static constexpr int NS = 4;              // LDS stages
     static constexpr int NR = NR_;            // tiles in flight in registers per wave
@@ -663,16 +664,17 @@ struct WideCfg {
     static constexpr int US = US_;                          // units of an 8-row group a score wave moves
     static constexpr int UV = 9 - US;                       // ... and its value-wave partner
     static constexpr int P_ROW = TT * 2;                    // bytes of one P^T row (bf16)
-    static constexpr int P_BYTES = RW * P_ROW;              // P^T of one tile
+    static constexpr int P_BYTES = 64 * P_ROW;              // P^T of one tile (room for 64 rows)
     static constexpr int OFF_P = NS * LDS_TILE;
-    static constexpr int OFF_ALPHA = OFF_P + 2 * P_BYTES;   // fp32 [2][RW] rescale factors
-    static constexpr int OFF_FLAG = OFF_ALPHA + 2 * RW * 4; // int [2][4] rescale flags
-    static constexpr int OFF_ML = OFF_FLAG + 2 * 4 * 4;     // fp32 [2][RW] final m, l
-    static constexpr int LDS_BYTES = OFF_ML + 2 * RW * 4;
+    static constexpr int OFF_ALPHA = OFF_P + 2 * P_BYTES;   // fp32 [2][64] rescale factors
+    static constexpr int OFF_FLAG = OFF_ALPHA + 2 * 64 * 4; // int [2][4] rescale flags
+    static constexpr int OFF_ML = OFF_FLAG + 2 * 4 * 4;     // fp32 [2][64] final m, l
+    static constexpr int LDS_BYTES = OFF_ML + 2 * 64 * 4;
     static constexpr int THREADS = NW * 64;
     static_assert(UNITS == 36, "four 8-row groups of nine 1-KiB units");
     static_assert(NR == 1 || NR == 2, "one or two tiles in flight per wave");
     static_assert(US >= 1 && US <= 9, "score waves move 1..9 units of their group");
+    static_assert(NRB == 2 || NRB == 4, "32 or 64 rows per workgroup");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
@@ -708,7 +710,7 @@ __global__ void __launch_bounds__(C::THREADS) split_wide_kernel(FwdArgs a)
 
     const int row_base = rg * C::RW;                  // first row of this group
     const int srow = row_base + 16 * w4 + lr;         // score waves: this lane's row
-    const int qi = row_base / a.heads;                // the group's query token (heads % 64 == 0)
+    const int qi = (row_base + 16 * w4) / a.heads;    // score waves: query token of the row block
     const bool bad_seq = (L != plan_L) || L < 0 || (long long)L > (long long)kPage * a.bt_stride;
     if (bad_seq) {
         if (tid < C::RW) lse_part[row_base + tid] = __builtin_nanf("");
@@ -866,7 +868,16 @@ __global__ void __launch_bounds__(C::THREADS) split_wide_kernel(FwdArgs a)
     };
 
     constexpr float kLazyRescale = 8.f;
-    if (is_score) {
+    if (is_score && w4 >= C::NRB) {
+        // ================= staging only (score waves without rows) =================
+        run_pipeline(
+            Idx<C::US>{}, Idx<0>{}, [&]() __attribute__((always_inline)) {},
+            [&](int t, auto full, auto&& slot_fn) __attribute__((always_inline)) {
+#pragma unroll
+                for (int j = 0; j < 2 * C::US; ++j) slot_fn(j);
+            },
+            [&]() __attribute__((always_inline)) { __syncthreads(); });
+    } else if (is_score) {
         // ================= score role =================
         bf16x8 qop[kKSteps];
         {
@@ -932,7 +943,7 @@ __global__ void __launch_bounds__(C::THREADS) split_wide_kernel(FwdArgs a)
                         const float alpha = (m_new == -__builtin_inff()) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
                         m_run = m_new;
                         l_run *= alpha;
-                        alpha_s[par * C::RW + 16 * w4 + lr] = alpha;   // the four lanes of a row agree
+                        alpha_s[par * 64 + 16 * w4 + lr] = alpha;   // the four lanes of a row agree
                         flag_s[par * 4 + w4] = resc ? 1 : 0;
                     }
                     if (j == 7 || j == 9) {   // probabilities of one 16-token block
@@ -971,7 +982,7 @@ __global__ void __launch_bounds__(C::THREADS) split_wide_kernel(FwdArgs a)
                 l_run = wave_sum_groups(l_run);
                 if (lg == 0) {
                     ml_s[16 * w4 + lr] = m_run;
-                    ml_s[C::RW + 16 * w4 + lr] = l_run;
+                    ml_s[64 + 16 * w4 + lr] = l_run;
                     lse_part[srow] = bad_page ? __builtin_nanf("")
                                               : (l_run > 0.f ? (m_run + __builtin_amdgcn_logf(l_run)) * kLn2
                                                              : -__builtin_inff());
@@ -981,24 +992,25 @@ __global__ void __launch_bounds__(C::THREADS) split_wide_kernel(FwdArgs a)
     } else {
         // ================= value role =================
         // acc[dt][rb] holds O^T[SEG w4 + 16 dt + 4 lg + i][row_base + 16 rb + lr]
-        f32x4 acc[C::DTW][4];
+        constexpr int NRB = C::NRB;
+        f32x4 acc[C::DTW][NRB];
 #pragma unroll
         for (int dt = 0; dt < C::DTW; ++dt)
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb) acc[dt][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int rb = 0; rb < NRB; ++rb) acc[dt][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
         constexpr int VD = 2;   // V-operand look-ahead (16-dim tiles of four MFMAs)
         auto value_step = [&](int tv, bool do_v, auto&& slot_fn) __attribute__((always_inline)) {
             const char* vt0 = smem + (tv % C::NS) * C::LDS_TILE + vbase;
-            bf16x8 pop[4];
+            bf16x8 pop[NRB];
             i16x4 vlo[VD + 1], vhi[VD + 1];
             if (do_v) {
                 const int par = tv & 1;
                 // rows of a block that took a new max in tile tv: rescale their accumulators
                 const i32x4 flags = *reinterpret_cast<const i32x4*>(flag_s + par * 4);
 #pragma unroll
-                for (int rb = 0; rb < 4; ++rb) {
+                for (int rb = 0; rb < NRB; ++rb) {
                     if (__builtin_amdgcn_readfirstlane(flags[rb]) != 0) {
-                        const float al = alpha_s[par * C::RW + 16 * rb + lr];
+                        const float al = alpha_s[par * 64 + 16 * rb + lr];
 #pragma unroll
                         for (int dt = 0; dt < C::DTW; ++dt) {
                             acc[dt][rb] *= al;
@@ -1008,7 +1020,7 @@ __global__ void __launch_bounds__(C::THREADS) split_wide_kernel(FwdArgs a)
                 }
                 const char* pb = pbuf0 + par * C::P_BYTES;
 #pragma unroll
-                for (int rb = 0; rb < 4; ++rb) pop[rb] = kread(pb + (16 * rb + lr) * C::P_ROW + pchunk);
+                for (int rb = 0; rb < NRB; ++rb) pop[rb] = kread(pb + (16 * rb + lr) * C::P_ROW + pchunk);
 #pragma unroll
                 for (int d = 0; d < VD; ++d) {
                     vlo[d] = vread(vt0 + 32 * d);
@@ -1026,7 +1038,7 @@ __global__ void __launch_bounds__(C::THREADS) split_wide_kernel(FwdArgs a)
                                                                __builtin_bit_cast(bf16x4, vhi[dt % (VD + 1)]),
                                                                0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-                    for (int rb = 0; rb < 4; ++rb)
+                    for (int rb = 0; rb < NRB; ++rb)
                         acc[dt][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[rb], acc[dt][rb], 0, 0, 0);
                 }
                 slot_fn(dt);
@@ -1046,8 +1058,8 @@ __global__ void __launch_bounds__(C::THREADS) split_wide_kernel(FwdArgs a)
                 if (n_tiles > 0) value_step(n_tiles - 1, true, [](int) {});   // value of the last tile
                 __syncthreads();
 #pragma unroll
-                for (int rb = 0; rb < 4; ++rb) {
-                    const float l = ml_s[C::RW + 16 * rb + lr];
+                for (int rb = 0; rb < NRB; ++rb) {
+                    const float l = ml_s[64 + 16 * rb + lr];
                     const float inv = (l > 0.f) ? 1.f / l : 0.f;
                     float* orow = o_part + (size_t)(row_base + 16 * rb + lr) * kDv + C::SEG * w4;
 #pragma unroll
