@@ -285,6 +285,14 @@ struct PageWindow {
     }
 };
 
+// Partial outputs are written once and read once by the combine kernel on whichever XCD it runs:
+// streaming (non-temporal) stores send them on to memory during the kernel instead of leaving
+// them dirty in this XCD's L2 for the write-back at the kernel's end.
+__device__ inline void store_partial(float* p, f32x4 v)
+{
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+}
+
 template <int B>
 struct Idx {
     static constexpr int value = B;
@@ -581,7 +589,7 @@ __global__ void __launch_bounds__(C::THREADS) split_kernel(FwdArgs a)
         float* orow = o_part + (size_t)out_row * kDv + 16 * dt0;
 #pragma unroll
         for (int dt = 0; dt < C::DTW; ++dt)
-            *reinterpret_cast<f32x4*>(orow + 16 * dt + 4 * lg) = acc[dt] * inv;
+            store_partial(orow + 16 * dt + 4 * lg, acc[dt] * inv);
         if (lg == 0 && dsi == 0)
             lse_part[out_row] = bad_page ? __builtin_nanf("")
                                          : (l_run > 0.f ? (m_run + __builtin_amdgcn_logf(l_run)) * kLn2
@@ -621,7 +629,7 @@ __global__ void __launch_bounds__(C::THREADS) split_kernel(FwdArgs a)
             const float inv = (Lsum > 0.f) ? 1.f / Lsum : 0.f;
             const int rbi = w0 / C::DS, seg = w0 % C::DS;
             const int grow = (blockIdx.y * C::RB + rbi) * 16 + r;
-            *reinterpret_cast<f32x4*>(o_part + (size_t)grow * kDv + seg * SEG + 4 * d4) = o * inv;
+            store_partial(o_part + (size_t)grow * kDv + seg * SEG + 4 * d4, o * inv);
             if (d4 == 0 && seg == 0)
                 lse_part[grow] = nan ? __builtin_nanf("")
                                      : (Lsum > 0.f ? (M + __builtin_amdgcn_logf(Lsum)) * kLn2 : -__builtin_inff());
@@ -1064,7 +1072,7 @@ __global__ void __launch_bounds__(C::THREADS) split_wide_kernel(FwdArgs a)
                     float* orow = o_part + (size_t)(row_base + 16 * rb + lr) * kDv + C::SEG * w4;
 #pragma unroll
                     for (int dt = 0; dt < C::DTW; ++dt)
-                        *reinterpret_cast<f32x4*>(orow + 16 * dt + 4 * lg) = acc[dt][rb] * inv;
+                        store_partial(orow + 16 * dt + 4 * lg, acc[dt][rb] * inv);
                 }
             });
     }
@@ -1078,6 +1086,8 @@ __global__ void __launch_bounds__(C::THREADS) split_wide_kernel(FwdArgs a)
 // =============================================================================================
 constexpr int kCombineThreads = 128;   // one (sequence, row) per workgroup, 4 dims per thread
 constexpr int kCombineChunk = 512;     // split weights staged in LDS per pass
+
+constexpr int kCombineFast = 24;       // rows with at most this many splits: one memory round trip
 
 __global__ void __launch_bounds__(kCombineThreads) combine_kernel(FwdArgs a)
 {
@@ -1100,18 +1110,32 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(FwdArgs a)
         s0 = bs[b];
         s1 = bs[b + 1];
     }
+    const int n = s1 - s0;
     const float* lse_part = reinterpret_cast<const float*>(a.ws + lay.lse_part);
     const float* o_part = reinterpret_cast<const float*>(a.ws + lay.o_part);
+    const float* op = o_part + ((size_t)s0 * a.rows + r) * kDv + 4 * t;   // split s0, this thread's dims
+    const size_t stride = (size_t)a.rows * kDv;                           // between splits
 
     __shared__ float w[kCombineChunk];
     __shared__ float red_m[kCombineThreads / 64];
     __shared__ int red_nan[kCombineThreads / 64];
 
-    // pass 1: M = max_s LSE_s (NaN anywhere poisons the row)
+    // few splits: issue every partial-row load together with the LSE loads, before any wait
+    const bool fast = n <= kCombineFast;
+    f32x4 ov[kCombineFast];
+    if (fast) {
+#pragma unroll
+        for (int i = 0; i < kCombineFast; ++i)
+            if (i < n) ov[i] = *reinterpret_cast<const f32x4*>(op + i * stride);
+    }
+
+    // M = max_s LSE_s (NaN anywhere poisons the row)
     float M = -__builtin_inff();
     int nan = 0;
+    float my_lse = -__builtin_inff();   // fast path: thread t < n holds LSE of split s0 + t
     for (int s = s0 + t; s < s1; s += kCombineThreads) {
         const float v = lse_part[(size_t)s * a.rows + r];
+        if (s == s0 + t) my_lse = v;
         nan |= (v != v);
         M = fmaxf(M, v);
     }
@@ -1131,28 +1155,38 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(FwdArgs a)
     }
     poison |= (nan != 0);
 
-    // pass 2: weights exp(LSE_s - M) through LDS, then the weighted sum of the partial rows
+    // weights exp(LSE_s - M) through LDS, then the weighted sum of the partial rows
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
     float W = 0.f;
-    if (!poison && M != -__builtin_inff()) {
+    if (fast) {
+        if (t < n) w[t] = (poison || M == -__builtin_inff()) ? 0.f : expf(my_lse - M);
+        __syncthreads();
+        if (!poison && M != -__builtin_inff()) {
+#pragma unroll
+            for (int i = 0; i < kCombineFast; ++i)
+                if (i < n) {
+                    o += w[i] * ov[i];
+                    W += w[i];
+                }
+        }
+    } else if (!poison && M != -__builtin_inff()) {
         for (int c0 = s0; c0 < s1; c0 += kCombineChunk) {
-            const int n = min(kCombineChunk, s1 - c0);
+            const int nc = min(kCombineChunk, s1 - c0);
             __syncthreads();
-            for (int i = t; i < n; i += kCombineThreads) w[i] = expf(lse_part[(size_t)(c0 + i) * a.rows + r] - M);
+            for (int i = t; i < nc; i += kCombineThreads) w[i] = expf(lse_part[(size_t)(c0 + i) * a.rows + r] - M);
             __syncthreads();
-            const float* op = o_part + ((size_t)c0 * a.rows + r) * kDv + 4 * t;
-            const size_t stride = (size_t)a.rows * kDv;
+            const float* oc = op + (size_t)(c0 - s0) * stride;
             int i = 0;
-            for (; i + 4 <= n; i += 4) {
-                const f32x4 v0 = *reinterpret_cast<const f32x4*>(op + (i + 0) * stride);
-                const f32x4 v1 = *reinterpret_cast<const f32x4*>(op + (i + 1) * stride);
-                const f32x4 v2 = *reinterpret_cast<const f32x4*>(op + (i + 2) * stride);
-                const f32x4 v3 = *reinterpret_cast<const f32x4*>(op + (i + 3) * stride);
+            for (; i + 4 <= nc; i += 4) {
+                const f32x4 v0 = *reinterpret_cast<const f32x4*>(oc + (i + 0) * stride);
+                const f32x4 v1 = *reinterpret_cast<const f32x4*>(oc + (i + 1) * stride);
+                const f32x4 v2 = *reinterpret_cast<const f32x4*>(oc + (i + 2) * stride);
+                const f32x4 v3 = *reinterpret_cast<const f32x4*>(oc + (i + 3) * stride);
                 o += w[i] * v0 + w[i + 1] * v1 + w[i + 2] * v2 + w[i + 3] * v3;
                 W += (w[i] + w[i + 1]) + (w[i + 2] + w[i + 3]);
             }
-            for (; i < n; ++i) {
-                o += w[i] * *reinterpret_cast<const f32x4*>(op + i * stride);
+            for (; i < nc; ++i) {
+                o += w[i] * *reinterpret_cast<const f32x4*>(oc + i * stride);
                 W += w[i];
             }
         }
