@@ -857,7 +857,7 @@ __global__ void __launch_bounds__(C::THREADS) split_wide_kernel(FwdArgs a)
         };
         any_step(0, Idx<0>{});
         int t = 1;
-        if constexpr (NR == 2) {
+        if constexpr (NR == 2 && NU > 0) {
             for (; t + 3 + NR < n_tiles; t += 2) {   // steps t (odd) and t + 1 have every part
                 full_step(t, Idx<1>{});
                 full_step(t + 1, Idx<0>{});
