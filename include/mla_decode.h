@@ -129,6 +129,32 @@ int mla_decode_fwd_combine(const int32_t *seqlens, int bt_stride, int batch, int
                            int num_heads, void *workspace, size_t workspace_bytes, void *out,
                            float *lse, void *stream);
 
+/*
+ * The step before the decode path for the s_q new tokens of a decode step: append each token's
+ * latent cache row and rotate the 64-d RoPE parts (the cache row of the absorbed form is the
+ * 512-d latent plus one shared RoPE key, GQLA summary, section "Arquitetura").  For sequence b
+ * and new token i, pos = L_b - s_q + i; the row at page block_table[b][pos / 64], slot pos % 64
+ * of kv_cache receives kv_latent[b][i] unchanged in dims 0..511 and k_rope[b][i] rotated by pos
+ * in dims 512..575, and dims 512..575 of q[b][i][h] are rotated by pos in place for every head.
+ * Rotation (the rotary embedding in its original pairwise form, a reading: the pages do not give
+ * the formula): the pair (x[2p], x[2p+1]) of a 64-d part turns by pos * rope_base^(-2p/64),
+ * p = 0..31; it is evaluated in fp64 and rounded once to bf16 (nearest even).
+ *   kv_latent  bf16 [batch][s_q][512], device
+ *   k_rope     bf16 [batch][s_q][64], device, before rotation
+ *   q          bf16 [batch][s_q][num_heads][576], device, dims 512..575 rotated in place
+ *   kv_cache   bf16 [num_pages][64][576], device, one row written per new token
+ *   block_table, bt_stride, seqlens, num_pages, page_size: as for mla_decode_fwd
+ *   rope_base  finite, > 1 (e.g. 10000)
+ * Device-side input errors do not fault: a token whose pos is negative, whose L_b exceeds
+ * 64*bt_stride or whose page is outside [0, num_pages) writes no cache row and gets NaN in the
+ * rotated query dims of every head, so a following mla_decode_fwd reports it as NaN.
+ * Returns MLA_OK or an error code (nothing is launched on error).
+ */
+int mla_cache_append_rope(const void *kv_latent, const void *k_rope, void *q, void *kv_cache,
+                          const int32_t *block_table, int bt_stride, const int32_t *seqlens, int batch,
+                          int s_q, int num_heads, int num_pages, int page_size, float rope_base,
+                          void *stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char *mla_decode_status_string(int status);
 

@@ -14,6 +14,7 @@ Names follow the C ABI:
   * :func:`fwd_split`      -> ``mla_decode_fwd_split``   (first half of fwd)
   * :func:`fwd_combine`    -> ``mla_decode_fwd_combine`` (second half of fwd)
   * :func:`status_string`  -> ``mla_decode_status_string``
+  * :func:`cache_append_rope` -> ``mla_cache_append_rope`` (new tokens into the paged cache)
 plus :func:`decode`, which allocates the workspace/outputs and calls plan + fwd.
 """
 from __future__ import annotations
@@ -32,7 +33,7 @@ _LIB: ctypes.CDLL | None = None
 STATUS = {0: "MLA_OK", -1: "MLA_ERR_INVALID_ARG", -2: "MLA_ERR_UNSUPPORTED",
           -3: "MLA_ERR_WORKSPACE_TOO_SMALL", -4: "MLA_ERR_NO_DEVICE", -5: "MLA_ERR_HIP"}
 EXPORTS = ("mla_decode_workspace_size", "mla_decode_plan", "mla_decode_fwd", "mla_decode_fwd_split",
-           "mla_decode_fwd_combine", "mla_decode_status_string")
+           "mla_decode_fwd_combine", "mla_decode_status_string", "mla_cache_append_rope")
 
 
 class MlaDecodeError(RuntimeError):
@@ -61,6 +62,8 @@ def lib() -> ctypes.CDLL:
     L.mla_decode_fwd_split.restype = I
     L.mla_decode_fwd_combine.argtypes = [P, I, I, I, I, P, SZ, P, P, P]
     L.mla_decode_fwd_combine.restype = I
+    L.mla_cache_append_rope.argtypes = [P, P, P, P, P, I, P, I, I, I, I, I, ctypes.c_float, P]
+    L.mla_cache_append_rope.restype = I
     L.mla_decode_status_string.argtypes = [I]
     L.mla_decode_status_string.restype = ctypes.c_char_p
     _LIB = L
@@ -171,6 +174,31 @@ def fwd_combine(seqlens, bt_stride: int, s_q: int, num_heads: int, workspace, ou
     _check("mla_decode_fwd_combine", lib().mla_decode_fwd_combine(
         seqlens.data_ptr(), int(bt_stride), b, int(s_q), int(num_heads), workspace.data_ptr(), workspace.numel(),
         out.data_ptr(), lse.data_ptr(), _stream(stream)))
+
+
+def cache_append_rope(kv_latent, k_rope, q, kv_cache, block_table, seqlens, rope_base: float = 10000.0,
+                      stream=None) -> None:
+    """mla_cache_append_rope: write the s_q new tokens' cache rows (latent + rotated RoPE key) and
+    rotate the RoPE part of ``q`` in place."""
+    import torch
+    _require(q, "q", torch.bfloat16, 4)
+    dev = q.device
+    _require(kv_latent, "kv_latent", torch.bfloat16, 3, dev)
+    _require(k_rope, "k_rope", torch.bfloat16, 3, dev)
+    _require(kv_cache, "kv_cache", torch.bfloat16, 3, dev)
+    _require(block_table, "block_table", torch.int32, 2, dev)
+    _require(seqlens, "seqlens", torch.int32, 1, dev)
+    b, s_q, h, dk = q.shape
+    if dk != D_K or kv_cache.shape[2] != D_K:
+        raise ValueError("q and kv_cache rows must be 576 wide")
+    if tuple(kv_latent.shape) != (b, s_q, D_V) or tuple(k_rope.shape) != (b, s_q, D_K - D_V):
+        raise ValueError("kv_latent must be [b, s_q, 512] and k_rope [b, s_q, 64]")
+    if block_table.shape[0] != b or seqlens.shape[0] != b:
+        raise ValueError("block_table and seqlens need one row per sequence")
+    _check("mla_cache_append_rope", lib().mla_cache_append_rope(
+        kv_latent.data_ptr(), k_rope.data_ptr(), q.data_ptr(), kv_cache.data_ptr(), block_table.data_ptr(),
+        block_table.shape[1], seqlens.data_ptr(), b, s_q, h, kv_cache.shape[0], kv_cache.shape[1], float(rope_base),
+        _stream(stream)))
 
 
 def decode(q, kv_cache, block_table, seqlens, softmax_scale: float, causal: bool = False, workspace=None,

@@ -9,6 +9,7 @@
 #include <cstring>
 #include <mutex>
 
+#include "mla_append_kernels.h"
 #include "mla_decode_kernels.h"
 
 namespace {
@@ -274,6 +275,38 @@ int mla_decode_fwd_combine(const int32_t* seqlens, int bt_stride, int batch, int
                                &g);
     if (st != MLA_OK) return st;
     return launch_combine(a, static_cast<hipStream_t>(stream));
+}
+
+int mla_cache_append_rope(const void* kv_latent, const void* k_rope, void* q, void* kv_cache,
+                          const int32_t* block_table, int bt_stride, const int32_t* seqlens, int batch, int s_q,
+                          int num_heads, int num_pages, int page_size, float rope_base, void* stream)
+{
+    if (!kv_latent || !k_rope || !q || !kv_cache || !block_table || !seqlens) return MLA_ERR_INVALID_ARG;
+    if (batch < 1 || bt_stride < 1 || num_pages < 1) return MLA_ERR_INVALID_ARG;
+    if (!std::isfinite(rope_base) || !(rope_base > 1.f)) return MLA_ERR_INVALID_ARG;
+    if (!aligned(kv_latent, 16) || !aligned(k_rope, 4) || !aligned(q, 4) || !aligned(kv_cache, 16) ||
+        !aligned(block_table, 4) || !aligned(seqlens, 4))
+        return MLA_ERR_INVALID_ARG;
+    if (!heads_ok(s_q, num_heads) || page_size != MLA_DECODE_PAGE_SIZE) return MLA_ERR_UNSUPPORTED;
+    const DeviceInfo* d = nullptr;
+    const int st = device_info(&d);
+    if (st != MLA_OK) return st;
+    AppendArgs a;
+    a.kv_latent = static_cast<const uint16_t*>(kv_latent);
+    a.k_rope = static_cast<const uint16_t*>(k_rope);
+    a.q = static_cast<uint16_t*>(q);
+    a.cache = static_cast<uint16_t*>(kv_cache);
+    a.block_table = block_table;
+    a.seqlens = seqlens;
+    a.num_pages = num_pages;
+    a.bt_stride = bt_stride;
+    a.batch = batch;
+    a.s_q = s_q;
+    a.heads = num_heads;
+    a.log2_base = std::log2((double)rope_base);
+    hipLaunchKernelGGL(append_rope_kernel, dim3(batch * s_q), dim3(kAppendThreads), 0,
+                       static_cast<hipStream_t>(stream), a);
+    return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
 const char* mla_decode_status_string(int status)

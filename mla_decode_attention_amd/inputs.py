@@ -153,3 +153,13 @@ def make_case(name: str, batch: int, s_q: int, heads: int, seqlen, seed: int, *,
                       softmax_scale=float(softmax_scale), seed=seed,
                       meta=dict(pool_pages=pool, outlier_frac=outlier_frac,
                                 outlier_scale=outlier_scale))
+
+
+def make_append_inputs(case: DecodeCase, seed: int):
+    """Seeded inputs of the cache-append step for the s_q new tokens of `case`: the latent rows
+    (bf16 [b, s_q, 512]) and the RoPE keys before rotation (bf16 [b, s_q, 64]), N(0, 1) drawn in
+    fp32 and rounded to bf16 (nearest even)."""
+    rng = np.random.default_rng(seed)
+    lat = rng.standard_normal((case.batch, case.s_q, D_V), dtype=np.float32)
+    rope = rng.standard_normal((case.batch, case.s_q, D_K - D_V), dtype=np.float32)
+    return f32_to_bf16_bits(lat), f32_to_bf16_bits(rope)

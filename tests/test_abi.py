@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "mla_decode.h")
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(mla_decode_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(mla_\w+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -94,6 +94,25 @@ def test_workspace_size_argument_errors(L):
     assert L.mla_decode_workspace_size(1, 2, 48, ctypes.byref(n)) == -2
 
 
+def _append(L, **kw):
+    args = dict(lat=FAKE, rope=FAKE, q=FAKE, kv=FAKE, bt=FAKE, bt_stride=4, sl=FAKE, batch=1, s_q=1, heads=16,
+                num_pages=4, page_size=64, base=10000.0)
+    args.update(kw)
+    return L.mla_cache_append_rope(P(args["lat"]), P(args["rope"]), P(args["q"]), P(args["kv"]), P(args["bt"]),
+                                   args["bt_stride"], P(args["sl"]), args["batch"], args["s_q"], args["heads"],
+                                   args["num_pages"], args["page_size"], ctypes.c_float(args["base"]), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(lat=0), -1), (dict(rope=0), -1), (dict(q=0), -1), (dict(kv=0), -1), (dict(bt=0), -1), (dict(sl=0), -1),
+    (dict(batch=0), -1), (dict(bt_stride=0), -1), (dict(num_pages=0), -1), (dict(base=1.0), -1),
+    (dict(base=float("nan")), -1), (dict(base=float("inf")), -1), (dict(lat=FAKE + 8), -1), (dict(q=FAKE + 2), -1),
+    (dict(heads=8), -2), (dict(s_q=3), -2), (dict(page_size=128), -2),
+])
+def test_append_argument_errors(L, kw, code):
+    assert _append(L, **kw) == code
+
+
 def test_valid_arguments_without_a_gpu_report_no_device(L):
     import torch
     if torch.cuda.is_available():
@@ -102,5 +121,6 @@ def test_valid_arguments_without_a_gpu_report_no_device(L):
     assert L.mla_decode_workspace_size(16, 1, 16, ctypes.byref(n)) == -4
     assert L.mla_decode_plan(P(FAKE), 1, 1, 16, P(FAKE), 1 << 20, None) == -4
     assert _fwd(L) == -4
+    assert _append(L) == -4
     with pytest.raises(mla.MlaDecodeError):
         mla.workspace_size(16, 1, 16)

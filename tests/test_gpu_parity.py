@@ -13,16 +13,6 @@ from gpu_helpers import log, parity, run_gpu, to_device
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(scope="module")
-def dev():
-    import torch
-    if not torch.cuda.is_available():
-        pytest.skip("no GPU")
-    import mla_decode_attention_amd as mla
-    mla.lib()
-    return torch.device("cuda:0")
-
-
 def full_parity(case, dev, what=None):
     what = what or case.name
     log(f"case {what}: b={case.batch} s_q={case.s_q} h={case.heads} L={case.seqlens.tolist()[:6]} "
