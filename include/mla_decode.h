@@ -130,6 +130,35 @@ int mla_decode_fwd_combine(const int32_t *seqlens, int bt_stride, int batch, int
                            float *lse, void *stream);
 
 /*
+ * Sparse (top-k) decode: every head of query token (b, i) attends exactly the cache rows that
+ * token's index list names instead of all L_b rows (GQLA summary, section "GQLA Esparso":
+ * fine-grained sparse attention over the latent cache; how the rows are selected is an input).
+ * With the rows j listed for (b, i):
+ *     s_j = softmax_scale * dot(q[b,i,h,0:576], k_j),  LSE = ln sum_j exp(s_j),
+ *     O = sum_j exp(s_j - LSE) * k_j[0:512].
+ * Each query token is its own split-KV sequence of topk index slots, so the plan depends only on
+ * (batch, s_q, num_heads, topk) and one plan serves every layer and step with that shape.
+ *   num_heads  16 (one GPU's share of 128); s_q 1 or 2; topk >= 1
+ *   indices    int32 [batch][s_q][topk], device: logical token positions of sequence b (its row
+ *              is page block_table[b][j / 64], slot j % 64); -1 marks an unused slot; a position
+ *              listed twice counts as two keys
+ *   other arguments as for mla_decode_fwd (there is no causal flag: the lists decide)
+ * Device-side input errors do not fault: a token with an index outside [0, L_b), or whose row
+ * lies on a page outside [0, num_pages), or whose sequence has L_b outside [0, 64*bt_stride],
+ * gets NaN in every out/lse element of that token; a token with no index gets O = 0, LSE = -inf.
+ */
+int mla_sparse_decode_workspace_size(int batch, int s_q, int num_heads, int topk, size_t *bytes);
+
+int mla_sparse_decode_plan(int batch, int s_q, int num_heads, int topk, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+int mla_sparse_decode_fwd(const void *q, const void *kv_cache, const int32_t *block_table,
+                          int bt_stride, const int32_t *seqlens, const int32_t *indices, int batch,
+                          int s_q, int num_heads, int topk, int num_pages, int page_size,
+                          float softmax_scale, void *workspace, size_t workspace_bytes, void *out,
+                          float *lse, void *stream);
+
+/*
  * The step before the decode path for the s_q new tokens of a decode step: append each token's
  * latent cache row and rotate the 64-d RoPE parts (the cache row of the absorbed form is the
  * 512-d latent plus one shared RoPE key, GQLA summary, section "Arquitetura").  For sequence b

@@ -15,6 +15,8 @@ Names follow the C ABI:
   * :func:`fwd_combine`    -> ``mla_decode_fwd_combine`` (second half of fwd)
   * :func:`status_string`  -> ``mla_decode_status_string``
   * :func:`cache_append_rope` -> ``mla_cache_append_rope`` (new tokens into the paged cache)
+  * :func:`sparse_workspace_size`, :func:`sparse_plan`, :func:`sparse_fwd` ->
+    ``mla_sparse_decode_workspace_size`` / ``_plan`` / ``_fwd`` (top-k decode)
 plus :func:`decode`, which allocates the workspace/outputs and calls plan + fwd.
 """
 from __future__ import annotations
@@ -33,7 +35,8 @@ _LIB: ctypes.CDLL | None = None
 STATUS = {0: "MLA_OK", -1: "MLA_ERR_INVALID_ARG", -2: "MLA_ERR_UNSUPPORTED",
           -3: "MLA_ERR_WORKSPACE_TOO_SMALL", -4: "MLA_ERR_NO_DEVICE", -5: "MLA_ERR_HIP"}
 EXPORTS = ("mla_decode_workspace_size", "mla_decode_plan", "mla_decode_fwd", "mla_decode_fwd_split",
-           "mla_decode_fwd_combine", "mla_decode_status_string", "mla_cache_append_rope")
+           "mla_decode_fwd_combine", "mla_decode_status_string", "mla_cache_append_rope",
+           "mla_sparse_decode_workspace_size", "mla_sparse_decode_plan", "mla_sparse_decode_fwd")
 
 
 class MlaDecodeError(RuntimeError):
@@ -64,6 +67,12 @@ def lib() -> ctypes.CDLL:
     L.mla_decode_fwd_combine.restype = I
     L.mla_cache_append_rope.argtypes = [P, P, P, P, P, I, P, I, I, I, I, I, ctypes.c_float, P]
     L.mla_cache_append_rope.restype = I
+    L.mla_sparse_decode_workspace_size.argtypes = [I, I, I, I, ctypes.POINTER(SZ)]
+    L.mla_sparse_decode_workspace_size.restype = I
+    L.mla_sparse_decode_plan.argtypes = [I, I, I, I, P, SZ, P]
+    L.mla_sparse_decode_plan.restype = I
+    L.mla_sparse_decode_fwd.argtypes = [P, P, P, I, P, P, I, I, I, I, I, I, ctypes.c_float, P, SZ, P, P, P]
+    L.mla_sparse_decode_fwd.restype = I
     L.mla_decode_status_string.argtypes = [I]
     L.mla_decode_status_string.restype = ctypes.c_char_p
     _LIB = L
@@ -199,6 +208,61 @@ def cache_append_rope(kv_latent, k_rope, q, kv_cache, block_table, seqlens, rope
         kv_latent.data_ptr(), k_rope.data_ptr(), q.data_ptr(), kv_cache.data_ptr(), block_table.data_ptr(),
         block_table.shape[1], seqlens.data_ptr(), b, s_q, h, kv_cache.shape[0], kv_cache.shape[1], float(rope_base),
         _stream(stream)))
+
+
+def sparse_workspace_size(batch: int, s_q: int, num_heads: int, topk: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check("mla_sparse_decode_workspace_size",
+           lib().mla_sparse_decode_workspace_size(int(batch), int(s_q), int(num_heads), int(topk), ctypes.byref(out)))
+    return int(out.value)
+
+
+def sparse_plan(batch: int, s_q: int, num_heads: int, topk: int, workspace, stream=None) -> None:
+    """mla_sparse_decode_plan: split metadata for this shape into ``workspace``."""
+    import torch
+    _require(workspace, "workspace", torch.uint8, 1)
+    _check("mla_sparse_decode_plan", lib().mla_sparse_decode_plan(int(batch), int(s_q), int(num_heads), int(topk),
+                                                                  workspace.data_ptr(), workspace.numel(),
+                                                                  _stream(stream)))
+
+
+def sparse_fwd(q, kv_cache, block_table, seqlens, indices, softmax_scale: float, workspace, out, lse,
+               stream=None) -> None:
+    """mla_sparse_decode_fwd: O and LSE of every head over the rows listed in ``indices`` [b, s_q, topk]."""
+    import torch
+    _require(q, "q", torch.bfloat16, 4)
+    dev = q.device
+    _require(kv_cache, "kv_cache", torch.bfloat16, 3, dev)
+    _require(block_table, "block_table", torch.int32, 2, dev)
+    _require(seqlens, "seqlens", torch.int32, 1, dev)
+    _require(indices, "indices", torch.int32, 3, dev)
+    _require(workspace, "workspace", torch.uint8, 1, dev)
+    _require(out, "out", torch.bfloat16, 4, dev)
+    _require(lse, "lse", torch.float32, 3, dev)
+    b, s_q, h, dk = q.shape
+    if dk != D_K or kv_cache.shape[2] != D_K:
+        raise ValueError("q and kv_cache rows must be 576 wide")
+    if tuple(indices.shape[:2]) != (b, s_q):
+        raise ValueError("indices must be [b, s_q, topk]")
+    if tuple(out.shape) != (b, s_q, h, D_V) or tuple(lse.shape) != (b, s_q, h):
+        raise ValueError("out must be [b, s_q, h, 512] and lse [b, s_q, h]")
+    _check("mla_sparse_decode_fwd", lib().mla_sparse_decode_fwd(
+        q.data_ptr(), kv_cache.data_ptr(), block_table.data_ptr(), block_table.shape[1], seqlens.data_ptr(),
+        indices.data_ptr(), b, s_q, h, indices.shape[2], kv_cache.shape[0], kv_cache.shape[1], float(softmax_scale),
+        workspace.data_ptr(), workspace.numel(), out.data_ptr(), lse.data_ptr(), _stream(stream)))
+
+
+def sparse_decode(q, kv_cache, block_table, seqlens, indices, softmax_scale: float, stream=None):
+    """Allocate the workspace and outputs, plan and run one sparse decode step."""
+    import torch
+    b, s_q, h, _ = q.shape
+    topk = indices.shape[2]
+    ws = torch.empty(sparse_workspace_size(b, s_q, h, topk), dtype=torch.uint8, device=q.device)
+    out = torch.empty((b, s_q, h, D_V), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((b, s_q, h), dtype=torch.float32, device=q.device)
+    sparse_plan(b, s_q, h, topk, ws, stream)
+    sparse_fwd(q, kv_cache, block_table, seqlens, indices, softmax_scale, ws, out, lse, stream)
+    return out, lse
 
 
 def decode(q, kv_cache, block_table, seqlens, softmax_scale: float, causal: bool = False, workspace=None,

@@ -26,7 +26,7 @@ using CfgR16 = SplitCfg<4, 1, 1, 16, 1, 1>;    // 4 independent waves, one 18 Ki
 using CfgW32 = WideCfg<1, 5, 2>;               // 32 rows per workgroup
 using CfgW64 = WideCfg<1, 5, 4>;               // 64 rows per workgroup (row groups of 64 above)
 
-enum CfgId { kR16 = 0, kW32, kW64, kNumCfg };
+enum CfgId { kR16 = 0, kW32, kW64, kS16, kNumCfg };   // kS16: sparse (gathered-row) form of kR16
 
 struct LaunchGeom {
     CfgId cfg;
@@ -53,6 +53,7 @@ const void* split_fn(CfgId c)
     switch (c) {
     case kR16: return reinterpret_cast<const void*>(&split_kernel<CfgR16>);
     case kW32: return reinterpret_cast<const void*>(&split_wide_kernel<CfgW32>);
+    case kS16: return reinterpret_cast<const void*>(&split_kernel<CfgR16, true>);
     default: return reinterpret_cast<const void*>(&split_wide_kernel<CfgW64>);
     }
 }
@@ -92,8 +93,9 @@ int device_info(const DeviceInfo** out)
             d.status = MLA_ERR_NO_DEVICE;   // the code objects are built for gfx950 only
         } else {
             d.num_cu = prop.multiProcessorCount;
-            static const int threads[kNumCfg] = {CfgR16::THREADS, CfgW32::THREADS, CfgW64::THREADS};
-            static const int lds[kNumCfg] = {CfgR16::LDS_BYTES, CfgW32::LDS_BYTES, CfgW64::LDS_BYTES};
+            static const int threads[kNumCfg] = {CfgR16::THREADS, CfgW32::THREADS, CfgW64::THREADS, CfgR16::THREADS};
+            static const int lds[kNumCfg] = {CfgR16::LDS_BYTES, CfgW32::LDS_BYTES, CfgW64::LDS_BYTES,
+                                             CfgR16::LDS_BYTES};
             for (int c = 0; c < kNumCfg; ++c) {
                 const void* fn = split_fn(static_cast<CfgId>(c));
                 int occ = 0;
@@ -165,7 +167,7 @@ int mla_decode_plan(const int32_t* seqlens, int batch, int s_q, int num_heads, v
     const int cap = item_capacity(*d, g, batch);
     if (workspace_bytes < ws_layout(batch, s_q * num_heads, cap).total) return MLA_ERR_WORKSPACE_TOO_SMALL;
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, static_cast<hipStream_t>(stream), seqlens,
-                       batch, s_q, num_heads, s_q * num_heads, gx_of(*d, g), cap, static_cast<char*>(workspace));
+                       batch, s_q, num_heads, s_q * num_heads, gx_of(*d, g), cap, static_cast<char*>(workspace), -1);
     return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -307,6 +309,104 @@ int mla_cache_append_rope(const void* kv_latent, const void* k_rope, void* q, vo
     hipLaunchKernelGGL(append_rope_kernel, dim3(batch * s_q), dim3(kAppendThreads), 0,
                        static_cast<hipStream_t>(stream), a);
     return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+namespace {
+
+// Sparse decode: each of the batch * s_q query tokens is a sequence of `topk` index slots with
+// num_heads (16) rows; the plan, the split workspace and the combine work per query token.
+constexpr LaunchGeom kSparseGeom = {kS16, 1, CfgR16::THREADS, CfgR16::LDS_BYTES};
+
+int sparse_shape_ok(int batch, int s_q, int num_heads, int topk)
+{
+    if (batch < 1 || topk < 1) return MLA_ERR_INVALID_ARG;
+    if ((s_q != 1 && s_q != 2) || num_heads != 16) return MLA_ERR_UNSUPPORTED;
+    if ((long long)batch * s_q > (1 << 24)) return MLA_ERR_INVALID_ARG;
+    return MLA_OK;
+}
+
+}  // namespace
+
+int mla_sparse_decode_workspace_size(int batch, int s_q, int num_heads, int topk, size_t* bytes)
+{
+    if (!bytes) return MLA_ERR_INVALID_ARG;
+    int st = sparse_shape_ok(batch, s_q, num_heads, topk);
+    if (st != MLA_OK) return st;
+    const DeviceInfo* d = nullptr;
+    st = device_info(&d);
+    if (st != MLA_OK) return st;
+    const int nt = batch * s_q;
+    *bytes = ws_layout(nt, num_heads, item_capacity(*d, kSparseGeom, nt)).total;
+    return MLA_OK;
+}
+
+int mla_sparse_decode_plan(int batch, int s_q, int num_heads, int topk, void* workspace, size_t workspace_bytes,
+                           void* stream)
+{
+    if (!workspace || !aligned(workspace, 256)) return MLA_ERR_INVALID_ARG;
+    int st = sparse_shape_ok(batch, s_q, num_heads, topk);
+    if (st != MLA_OK) return st;
+    const DeviceInfo* d = nullptr;
+    st = device_info(&d);
+    if (st != MLA_OK) return st;
+    const int nt = batch * s_q;
+    const int cap = item_capacity(*d, kSparseGeom, nt);
+    if (workspace_bytes < ws_layout(nt, num_heads, cap).total) return MLA_ERR_WORKSPACE_TOO_SMALL;
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, static_cast<hipStream_t>(stream), nullptr, nt,
+                       1, num_heads, num_heads, gx_of(*d, kSparseGeom), cap, static_cast<char*>(workspace), topk);
+    return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int mla_sparse_decode_fwd(const void* q, const void* kv_cache, const int32_t* block_table, int bt_stride,
+                          const int32_t* seqlens, const int32_t* indices, int batch, int s_q, int num_heads,
+                          int topk, int num_pages, int page_size, float softmax_scale, void* workspace,
+                          size_t workspace_bytes, void* out, float* lse, void* stream)
+{
+    if (!q || !kv_cache || !block_table || !seqlens || !indices || !workspace || !out || !lse)
+        return MLA_ERR_INVALID_ARG;
+    if (bt_stride < 1 || num_pages < 1 || !std::isfinite(softmax_scale)) return MLA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(block_table, 4) || !aligned(seqlens, 4) ||
+        !aligned(indices, 4) || !aligned(workspace, 256) || !aligned(out, 8) || !aligned(lse, 4))
+        return MLA_ERR_INVALID_ARG;
+    int st = sparse_shape_ok(batch, s_q, num_heads, topk);
+    if (st != MLA_OK) return st;
+    if (page_size != MLA_DECODE_PAGE_SIZE) return MLA_ERR_UNSUPPORTED;
+    const DeviceInfo* d = nullptr;
+    st = device_info(&d);
+    if (st != MLA_OK) return st;
+    const int nt = batch * s_q;
+    const int cap = item_capacity(*d, kSparseGeom, nt);
+    const WsLayout lay = ws_layout(nt, num_heads, cap);
+    if (workspace_bytes < lay.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
+    FwdArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.cache = static_cast<const uint16_t*>(kv_cache);
+    a.block_table = block_table;
+    a.seqlens = seqlens;
+    a.ws = static_cast<char*>(workspace);
+    a.out = static_cast<uint16_t*>(out);
+    a.lse = lse;
+    a.num_pages = num_pages;
+    a.bt_stride = bt_stride;
+    a.batch = nt;
+    a.s_q = 1;
+    a.heads = num_heads;
+    a.rows = num_heads;
+    a.capacity = cap;
+    a.scale_log2 = softmax_scale * kLog2e;
+    a.causal = 0;
+    a.row_groups = 1;
+    a.indices = indices;
+    a.topk = topk;
+    a.sparse_sq = s_q;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipLaunchKernelGGL((split_kernel<CfgR16, true>), dim3(cap, 1), dim3(CfgR16::THREADS), CfgR16::LDS_BYTES, s, a);
+    if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
+    // the combine checks each token's length against the plan's copy of it and the table width
+    FwdArgs c = a;
+    c.seqlens = reinterpret_cast<const int32_t*>(a.ws + lay.seqlens);
+    c.bt_stride = (topk + kPage - 1) / kPage;
+    return launch_combine(c, s);
 }
 
 const char* mla_decode_status_string(int status)

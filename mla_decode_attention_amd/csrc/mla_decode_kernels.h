@@ -83,10 +83,13 @@ constexpr int kPlanThreads = 1024;
 
 __device__ inline int pages_of(int L) { return L <= 0 ? 0 : (L + kPage - 1) / kPage; }
 
+// uniform_len >= 0: every sequence has that length and `seqlens` is not read (sparse decode: each
+// query token is a sequence of top-k index slots)
 __global__ void __launch_bounds__(kPlanThreads) plan_kernel(const int32_t* __restrict__ seqlens, int batch,
                                                             int s_q, int heads, int rows, int gx,
-                                                            int capacity, char* __restrict__ ws)
+                                                            int capacity, char* __restrict__ ws, int uniform_len)
 {
+    auto len_of = [&](int b) { return uniform_len >= 0 ? uniform_len : seqlens[b]; };
     const WsLayout lay = ws_layout(batch, rows, capacity);
     int32_t* header = reinterpret_cast<int32_t*>(ws + lay.header);
     int32_t* ws_len = reinterpret_cast<int32_t*>(ws + lay.seqlens);
@@ -101,7 +104,7 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(const int32_t* __res
     // total pages
     long long mine = 0;
     for (int b = tid; b < batch; b += kPlanThreads) {
-        const int L = seqlens[b];
+        const int L = len_of(b);
         ws_len[b] = L;
         mine += pages_of(L);
     }
@@ -119,7 +122,7 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(const int32_t* __res
         const int b = base + tid;
         int n = 0, pg = 0;
         if (b < batch) {
-            pg = pages_of(seqlens[b]);
+            pg = pages_of(len_of(b));
             n = int((pg + chunk - 1) / chunk);
         }
         int incl = n;
@@ -221,6 +224,11 @@ struct FwdArgs {
     float scale_log2;   // softmax_scale * log2(e)
     int causal;
     int row_groups;     // workgroups per work item (wide form)
+    // sparse (top-k) decode: each query token is a sequence of `topk` index slots; `batch` and
+    // `s_q` above then count query tokens (batch * sparse_sq) and 1
+    const int32_t* indices;   // int32 [b][sparse_sq][topk] logical token positions, -1 = unused
+    int topk;
+    int sparse_sq;
 };
 
 __device__ inline const MLA_LDS i16x4* lds_i16x4(const void* p)
@@ -298,7 +306,9 @@ struct Idx {
     static constexpr int value = B;
 };
 
-template <class C>
+// SPARSE: the keys of a sequence are the cache rows its index list names (gathered row by row)
+// instead of its first L_b rows; see the sparse entry point of the C ABI.
+template <class C, bool SPARSE = false>
 __global__ void __launch_bounds__(C::THREADS) split_kernel(FwdArgs a)
 {
     extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -321,21 +331,24 @@ __global__ void __launch_bounds__(C::THREADS) split_kernel(FwdArgs a)
     const int item = blockIdx.x;
     if (item >= header[kHItems]) return;
     const i32x4 it = reinterpret_cast<const i32x4*>(a.ws + lay.items)[item];
-    const int b = it[0];
-    const int L = a.seqlens[b];
+    const int b = it[0];              // sequence (sparse: query token b_real * sparse_sq + i)
     const int32_t plan_L = reinterpret_cast<const int32_t*>(a.ws + lay.seqlens)[b];
+    // dense: L = context length; sparse: L = index slots, Lc = the context the indices point into
+    const int b_tab = SPARSE ? b / a.sparse_sq : b;
+    const int Lc = a.seqlens[b_tab];
+    const int L = SPARSE ? a.topk : Lc;
     float* lse_part = reinterpret_cast<float*>(a.ws + lay.lse_part) + (size_t)item * a.rows;
     float* o_part = reinterpret_cast<float*>(a.ws + lay.o_part) + (size_t)item * a.rows * kDv;
 
     const int rb = blockIdx.y * C::RB + rbl;          // global 16-row block
     const int row0 = rb * 16;
     const int qi = row0 / a.heads;                    // query token of this block (heads % 16 == 0)
-    const bool bad_seq = (L != plan_L) || L < 0 || (long long)L > (long long)kPage * a.bt_stride;
+    const bool bad_seq = (L != plan_L) || L < 0 || Lc < 0 || (long long)Lc > (long long)kPage * a.bt_stride;
     if (bad_seq) {
         if (tid < C::RB * 16) lse_part[blockIdx.y * C::RB * 16 + tid] = __builtin_nanf("");
         return;
     }
-    const int n_vis = a.causal ? min(max(L - a.s_q + 1 + qi, 0), L) : L;
+    const int n_vis = (!SPARSE && a.causal) ? min(max(L - a.s_q + 1 + qi, 0), L) : L;
     const int tok_begin = it[1] * kPage;
     const int tok_end = min(it[2] * kPage, L);
     const int n_tiles = (tok_end - tok_begin + C::TT - 1) / C::TT;
@@ -370,15 +383,65 @@ __global__ void __launch_bounds__(C::THREADS) split_kernel(FwdArgs a)
     const int unit0 = wg * C::NPW;                           // first unit of this wave
     char* const group_stages = smem + gi * C::NS * C::LDS_TILE;
     PageWindow pw;
-    pw.init(a.block_table + (size_t)b * a.bt_stride, a.bt_stride);
+    pw.init(a.block_table + (size_t)b_tab * a.bt_stride, a.bt_stride);
     bool bad_page = false;
 
     i32x4 rbuf[C::NR][C::NPW];
+    // sparse: validity masks (bit r = index slot r of the tile names a row) of the tiles loaded but
+    // not yet computed, oldest first; tile itn of the prologue goes to slot itn, later tiles to
+    // slot NR (each step shifts the queue after its compute)
+    uint32_t vmq[C::NR + 1] = {};
+    auto gather_tile = [&](int itn, int t0, auto buf_idx) {   // SPARSE only: rows of slots t0 .. t0+TT-1
+        constexpr int B = decltype(buf_idx)::value;
+        static_assert(C::TT == 16 && C::GW == 1, "the gather path takes one 16-token tile per wave");
+        int rowid = 0;      // lane r < 16: page * 64 + slot of the row of slot t0 + r
+        bool ok = false, bad = false;
+        if (lane < C::TT && t0 + lane < tok_end) {
+            const int idx = a.indices[(size_t)b * a.topk + t0 + lane];
+            if (idx >= 0) {
+                if (idx >= Lc) {
+                    bad = true;
+                } else {
+                    const int page = a.block_table[(size_t)b_tab * a.bt_stride + idx / kPage];
+                    if (page < 0 || (long long)page >= a.num_pages)
+                        bad = true;
+                    else {
+                        rowid = page * kPage + idx % kPage;
+                        ok = true;
+                    }
+                }
+            }
+        }
+        if (__builtin_amdgcn_ballot_w64(bad) != 0) bad_page = true;   // the whole token is poisoned
+        const uint32_t vmask = (uint32_t)__builtin_amdgcn_ballot_w64(ok);
+        if (itn <= 0)
+            vmq[0] = vmask;
+        else if (C::NR == 1 || itn == 1)
+            vmq[1] = vmask;
+        else
+            vmq[C::NR] = vmask;
+#pragma unroll
+        for (int kk = 0; kk < C::NPW; ++kk) {
+            const int c = 64 * (unit0 + kk) + lane;   // 16-B chunk of the tile
+            const int r = c / kChunksPerRow;
+            const int rid = __shfl(rowid, r);
+            if ((vmask >> r) & 1u) {
+                const i32x4* src = reinterpret_cast<const i32x4*>(a.cache + (size_t)rid * kDk) + (c - r * kChunksPerRow);
+                rbuf[B][kk] = __builtin_nontemporal_load(src);
+            } else {
+                rbuf[B][kk] = i32x4{0, 0, 0, 0};
+            }
+        }
+    };
     auto load_tile = [&](int itn, auto buf_idx) {
         constexpr int B = decltype(buf_idx)::value;
         const int k = itn * C::NG + gi;
         if (itn >= n_it || k >= n_tiles) return;
         const int t0 = tok_begin + k * C::TT;
+        if constexpr (SPARSE) {
+            gather_tile(itn, t0, buf_idx);
+            return;
+        }
         const int page = pw.page(t0 / kPage, lane);
         int valid = min(C::TT, L - t0);
         if (page < 0 || (long long)page >= a.num_pages) {
@@ -474,7 +537,16 @@ __global__ void __launch_bounds__(C::THREADS) split_kernel(FwdArgs a)
         // scale into the log2 domain, mask invisible tokens (only in a tile that crosses n_vis)
 #pragma unroll
         for (int st = 0; st < C::NST; ++st) s[st] *= a.scale_log2;
-        if (t0 + C::TT > n_vis) {
+        if constexpr (SPARSE) {
+            const uint32_t vm = vmq[0];
+            if (vm != (1u << C::TT) - 1u) {
+#pragma unroll
+                for (int st = 0; st < C::NST; ++st)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (!((vm >> (16 * st + 4 * lg + i)) & 1u)) s[st][i] = -__builtin_inff();
+            }
+        } else if (t0 + C::TT > n_vis) {
 #pragma unroll
             for (int st = 0; st < C::NST; ++st)
 #pragma unroll
@@ -563,6 +635,10 @@ __global__ void __launch_bounds__(C::THREADS) split_kernel(FwdArgs a)
         if (itn >= n_it) return;
         const int k = itn * C::NG + gi;
         if (k < n_tiles) compute_tile(itn, k);
+        if constexpr (SPARSE) {
+#pragma unroll
+            for (int i = 0; i < C::NR; ++i) vmq[i] = vmq[i + 1];
+        }
         store_tile(itn + 1, next_buf);
         load_tile(itn + 1 + C::NR, next_buf);
         if constexpr (C::GW > 1) __syncthreads();

@@ -163,3 +163,29 @@ def make_append_inputs(case: DecodeCase, seed: int):
     lat = rng.standard_normal((case.batch, case.s_q, D_V), dtype=np.float32)
     rope = rng.standard_normal((case.batch, case.s_q, D_K - D_V), dtype=np.float32)
     return f32_to_bf16_bits(lat), f32_to_bf16_bits(rope)
+
+
+def make_sparse_indices(case: DecodeCase, topk: int, seed: int, *, pad_frac: float = 0.0,
+                        duplicates: bool = False) -> np.ndarray:
+    """Seeded top-k index lists int32 [b, s_q, topk] for `case`: for each query token, min(topk, L_b)
+    distinct positions of its sequence drawn uniformly and shuffled; the remaining slots are -1.
+    `pad_frac` turns that fraction of the chosen slots into -1 at random places; `duplicates`
+    overwrites a quarter of the chosen slots with copies of others (a position listed twice)."""
+    rng = np.random.default_rng(seed)
+    out = np.full((case.batch, case.s_q, topk), -1, dtype=np.int32)
+    for b in range(case.batch):
+        L = int(case.seqlens[b])
+        for i in range(case.s_q):
+            n = min(topk, L)
+            if n <= 0:
+                continue
+            sel = rng.choice(L, size=n, replace=False).astype(np.int32)
+            if duplicates and n > 1:
+                m = max(1, n // 4)
+                sel[rng.choice(n, size=m, replace=False)] = sel[rng.integers(0, n, size=m)]
+            row = np.full(topk, -1, dtype=np.int32)
+            row[:n] = sel
+            if pad_frac > 0:
+                row[rng.random(topk) < pad_frac] = -1
+            out[b, i] = rng.permutation(row)
+    return out

@@ -17,6 +17,12 @@ Functions, each with the passage it follows:
   * :func:`transposed_attention` -- the ETAP ordering S^T = K Q^T,
     P^T = softmax(S^T) along the key axis, O = (V^T P^T)^T (summary, "Mecanismo
     Central", item 1), written with numpy fp64 matmuls as the steps.
+  * :func:`sparse_decode` -- top-k (sparse) decode: every head of a query token
+    attends exactly the cache rows its index list names (GQLA summary, "GQLA
+    Esparso": fine-grained sparse attention over the latent cache; the selection
+    is an input), i.e. :func:`attention` over a gathered key set.
+  * :mod:`oracle.rope_append` -- the cache append with rotary embedding of the
+    RoPE parts (the step that feeds the decode path).
   * :func:`merge_by_lse` -- merge of results over disjoint key subsets by their
     log-sum-exp; it is the exact identity softmax over a union of key sets
     obeys, used to pin split invariance.
@@ -124,6 +130,47 @@ def attention(q, k, v, scale: float, return_probs: bool = False):
 
 def mla_decode(q_bits, cache_bits, block_table, seqlens, scale, causal, d_v=512, rows=None, threads=None):
     return default().mla_decode(q_bits, cache_bits, block_table, seqlens, scale, causal, d_v, rows, threads)
+
+
+def _bf16_f64(bits) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def sparse_decode(q_bits, cache_bits, block_table, seqlens, indices, scale: float, d_v: int = 512,
+                  oracle: Oracle | None = None):
+    """fp64 O [b, s_q, h, d_v] and LSE [b, s_q, h] of the sparse decode step.
+
+    indices int [b, s_q, topk]: logical token positions of sequence b (cache row of position j:
+    page block_table[b][j // 64], slot j % 64); -1 marks an unused slot; a position listed twice is
+    two keys.  Every head of query token (b, i) attends the rows listed for (b, i).  A token with an
+    index outside [0, L_b) or whose row lies on a page outside the pool gets NaN; one with no index
+    gets O = 0, LSE = -inf.
+    """
+    orc = oracle or default()
+    q_bits = np.asarray(q_bits, dtype=np.uint16)
+    cache_bits = np.asarray(cache_bits, dtype=np.uint16)
+    bt = np.asarray(block_table, dtype=np.int64)
+    sl = np.asarray(seqlens, dtype=np.int64)
+    ind = np.asarray(indices, dtype=np.int64)
+    b, s_q, h, _ = q_bits.shape
+    num_pages, page = cache_bits.shape[:2]
+    o = np.zeros((b, s_q, h, d_v))
+    lse = np.full((b, s_q, h), -np.inf)
+    for bi in range(b):
+        for i in range(s_q):
+            idx = ind[bi, i]
+            idx = idx[idx >= 0]
+            if idx.size and (idx.max() >= sl[bi] or sl[bi] > page * bt.shape[1]):
+                o[bi, i], lse[bi, i] = np.nan, np.nan
+                continue
+            pages = bt[bi, idx // page]
+            if ((pages < 0) | (pages >= num_pages)).any():
+                o[bi, i], lse[bi, i] = np.nan, np.nan
+                continue
+            k = _bf16_f64(cache_bits[pages, idx % page])
+            oi, li = orc.attention(_bf16_f64(q_bits[bi, i]), k, k[:, :d_v], scale)
+            o[bi, i], lse[bi, i] = oi, li
+    return o, lse
 
 
 def transposed_attention(q, k, v, scale: float):

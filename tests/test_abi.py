@@ -113,6 +113,36 @@ def test_append_argument_errors(L, kw, code):
     assert _append(L, **kw) == code
 
 
+def _sparse_fwd(L, **kw):
+    args = dict(q=FAKE, kv=FAKE, bt=FAKE, bt_stride=4, sl=FAKE, ind=FAKE, batch=1, s_q=1, heads=16, topk=64,
+                num_pages=4, page_size=64, scale=0.07, ws=FAKE, ws_bytes=1 << 20, out=FAKE, lse=FAKE)
+    args.update(kw)
+    return L.mla_sparse_decode_fwd(P(args["q"]), P(args["kv"]), P(args["bt"]), args["bt_stride"], P(args["sl"]),
+                                   P(args["ind"]), args["batch"], args["s_q"], args["heads"], args["topk"],
+                                   args["num_pages"], args["page_size"], ctypes.c_float(args["scale"]), P(args["ws"]),
+                                   args["ws_bytes"], P(args["out"]), P(args["lse"]), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), -1), (dict(ind=0), -1), (dict(ws=0), -1), (dict(out=0), -1), (dict(batch=0), -1), (dict(topk=0), -1),
+    (dict(bt_stride=0), -1), (dict(num_pages=0), -1), (dict(scale=float("nan")), -1), (dict(ind=FAKE + 2), -1),
+    (dict(ws=FAKE + 64), -1), (dict(heads=32), -2), (dict(heads=128), -2), (dict(s_q=3), -2), (dict(page_size=16), -2),
+])
+def test_sparse_fwd_argument_errors(L, kw, code):
+    assert _sparse_fwd(L, **kw) == code
+
+
+def test_sparse_plan_and_size_argument_errors(L):
+    n = ctypes.c_size_t(0)
+    assert L.mla_sparse_decode_workspace_size(1, 1, 16, 64, None) == -1
+    assert L.mla_sparse_decode_workspace_size(0, 1, 16, 64, ctypes.byref(n)) == -1
+    assert L.mla_sparse_decode_workspace_size(1, 1, 16, 0, ctypes.byref(n)) == -1
+    assert L.mla_sparse_decode_workspace_size(1, 1, 64, 64, ctypes.byref(n)) == -2
+    assert L.mla_sparse_decode_plan(1, 1, 16, 64, None, 1 << 20, None) == -1
+    assert L.mla_sparse_decode_plan(1, 1, 16, 64, P(FAKE + 8), 1 << 20, None) == -1
+    assert L.mla_sparse_decode_plan(1, 3, 16, 64, P(FAKE), 1 << 20, None) == -2
+
+
 def test_valid_arguments_without_a_gpu_report_no_device(L):
     import torch
     if torch.cuda.is_available():
@@ -122,5 +152,7 @@ def test_valid_arguments_without_a_gpu_report_no_device(L):
     assert L.mla_decode_plan(P(FAKE), 1, 1, 16, P(FAKE), 1 << 20, None) == -4
     assert _fwd(L) == -4
     assert _append(L) == -4
+    assert _sparse_fwd(L) == -4
+    assert L.mla_sparse_decode_plan(1, 1, 16, 64, P(FAKE), 1 << 20, None) == -4
     with pytest.raises(mla.MlaDecodeError):
         mla.workspace_size(16, 1, 16)
