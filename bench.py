@@ -82,6 +82,68 @@ def cpu_baseline(case, o_gpu, lse_gpu, n_seqs: int, threads: int, min_seconds: f
                 seconds=round(dt, 2)), parity
 
 
+def measure_extras(mla, case, dev, q, cache, bt, sl, steps: int):
+    """Time the steps either side of the decode path on the same inputs: the cache append with
+    rotary embedding of the s_q new tokens, and a top-2048 sparse decode over the same cache (with
+    a parity check of sampled query tokens against the fp64 oracle)."""
+    import numpy as np
+    import torch
+
+    from mla_decode_attention_amd.inputs import make_append_inputs, make_sparse_indices
+    stream = torch.cuda.current_stream()
+    b, s_q, h = case.batch, case.s_q, case.heads
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / steps
+
+    out = {}
+    topk = 2048
+    ind = make_sparse_indices(case, topk, seed=8)
+    ind_d = torch.from_numpy(ind).to(dev)
+    ws = torch.empty(mla.sparse_workspace_size(b, s_q, h, topk), dtype=torch.uint8, device=dev)
+    o = torch.empty((b, s_q, h, 512), dtype=torch.bfloat16, device=dev)
+    l = torch.empty((b, s_q, h), dtype=torch.float32, device=dev)
+    mla.sparse_plan(b, s_q, h, topk, ws)
+    us = timed(lambda: mla.sparse_fwd(q, cache, bt, sl, ind_d, case.softmax_scale, ws, o, l))
+    nbytes = int((ind >= 0).sum()) * 1152 + b * s_q * h * 576 * 2
+    rec = {"us": round(us, 2), "topk": topk, "bytes": nbytes, "GB/s": round(nbytes / us / 1e3, 1),
+           "frac_of_hbm_peak": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4), "bound": "hbm"}
+    try:
+        import oracle
+        from mla_decode_attention_amd.inputs import bf16_bits_to_f32
+        og = bf16_bits_to_f32(o.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+        lg = l.cpu().numpy().astype(np.float64)
+        sel = [0, b - 1]
+        ro, rl = oracle.sparse_decode(case.q[sel], case.cache, case.block_table[sel], case.seqlens[sel], ind[sel],
+                                      case.softmax_scale)
+        err = np.abs(og[sel] - ro)
+        rec["parity_sampled_tokens"] = {"tokens": len(sel) * s_q, "o_maxabs": float(err.max()),
+                                        "lse_rel": float(np.max(np.abs(lg[sel] - rl) / np.maximum(1, np.abs(rl))))}
+    except Exception as exc:   # the timing stands without the check
+        rec["parity_sampled_tokens"] = f"skipped: {exc}"
+    out["sparse_topk2048"] = rec
+    # the append writes the new tokens' rows into the cache: measured after the sparse check
+    lat, rope = make_append_inputs(case, seed=7)
+    lat_d = torch.from_numpy(lat.view(np.int16)).to(dev).view(torch.bfloat16)
+    rope_d = torch.from_numpy(rope.view(np.int16)).to(dev).view(torch.bfloat16)
+    q2 = q.clone()
+    us = timed(lambda: mla.cache_append_rope(lat_d, rope_d, q2, cache, bt, sl))
+    nbytes = b * s_q * (512 * 2 + 64 * 2 + 576 * 2) + b * s_q * h * 64 * 2 * 2
+    out["append_rope"] = {"us": round(us, 2), "bytes": nbytes, "GB/s": round(nbytes / us / 1e3, 1),
+                          "bound": "launch", "tokens": b * s_q}
+
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -92,6 +154,7 @@ def main() -> int:
     ap.add_argument("--cpu-sample-seqs", type=int, default=16)
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (default: min(16, usable cores))")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum timed oracle work")
+    ap.add_argument("--no-extras", action="store_true", help="skip the append and sparse-decode timings")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this size (for scaling PMC byte counters)")
     args = ap.parse_args()
@@ -197,6 +260,12 @@ def main() -> int:
     o_gpu = bf16_bits_to_f32(out.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
     lse_gpu = lse.cpu().numpy().astype(np.float64)
 
+    extras = None
+    if not args.no_extras:
+        log("extras: cache append + RoPE, top-2048 sparse decode")
+        extras = measure_extras(mla, case, dev, q, cache, bt, sl, K)
+        log(f"extras: {extras}")
+
     cpu, parity = None, None
     if not args.no_cpu_baseline:
         try:
@@ -235,6 +304,7 @@ def main() -> int:
                      "mfma_frac": round(split_flops / (split_avg_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
         "cpu_baseline": cpu,
         "parity_vs_oracle": parity,
+        "extras": extras,
     }
     print(json.dumps(line), flush=True)
     return 0

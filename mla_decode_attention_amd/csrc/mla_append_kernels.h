@@ -48,12 +48,9 @@ __device__ inline uint16_t double_to_bf16_rne(double d)
     return (uint16_t)(u >> 16);
 }
 
-// rotate the bf16 pair at p[0], p[1] (pair index `pair` of the 64-d part) by position pos
-__device__ inline void rope_pair(const uint16_t* src, uint16_t* dst, int pair, int pos, double log2_base)
+// rotate the bf16 pair src[0], src[1] by the angle whose cosine and sine are c, s
+__device__ inline void rope_pair(const uint16_t* src, uint16_t* dst, double c, double s)
 {
-    const double theta = exp2(-(2.0 * pair / kRopeDim) * log2_base);
-    double s, c;
-    sincos((double)pos * theta, &s, &c);
     const double x = bf16_bits_to_double(src[0]);
     const double y = bf16_bits_to_double(src[1]);
     dst[0] = double_to_bf16_rne(x * c - y * s);
@@ -63,6 +60,7 @@ __device__ inline void rope_pair(const uint16_t* src, uint16_t* dst, int pair, i
 // One workgroup per new token (b, i).
 __global__ void __launch_bounds__(kAppendThreads) append_rope_kernel(AppendArgs a)
 {
+    __shared__ double cs[kRopeDim / 2][2];   // cos, sin of the token's angle for each pair
     const int tok = blockIdx.x;   // b * s_q + i
     const int b = tok / a.s_q;
     const int i = tok % a.s_q;
@@ -75,13 +73,21 @@ __global__ void __launch_bounds__(kAppendThreads) append_rope_kernel(AppendArgs 
         page = a.block_table[(size_t)b * a.bt_stride + pos / kPage];
         ok = page >= 0 && (long long)page < a.num_pages;
     }
+    if (ok && t < kRopeDim / 2) {
+        const double theta = exp2(-(2.0 * t / kRopeDim) * a.log2_base);
+        double s, c;
+        sincos((double)pos * theta, &s, &c);
+        cs[t][0] = c;
+        cs[t][1] = s;
+    }
+    __syncthreads();
     if (ok) {
         uint16_t* row = a.cache + ((size_t)page * kPage + pos % kPage) * kDk;
         if (t < kDv / 8) {   // latent: 64 x 16 B
             *reinterpret_cast<i32x4*>(row + 8 * t) = *reinterpret_cast<const i32x4*>(a.kv_latent + (size_t)tok * kDv + 8 * t);
         } else if (t < kDv / 8 + kRopeDim / 2) {
             const int p = t - kDv / 8;
-            rope_pair(a.k_rope + (size_t)tok * kRopeDim + 2 * p, row + kDv + 2 * p, p, pos, a.log2_base);
+            rope_pair(a.k_rope + (size_t)tok * kRopeDim + 2 * p, row + kDv + 2 * p, cs[p][0], cs[p][1]);
         }
     }
     // the query's RoPE part of every head; NaN when the token has no valid cache slot, so the
@@ -92,7 +98,7 @@ __global__ void __launch_bounds__(kAppendThreads) append_rope_kernel(AppendArgs 
         uint16_t* qr = a.q + ((size_t)tok * a.heads + h) * kDk + kDv + 2 * p;
         if (ok) {
             uint16_t r[2];
-            rope_pair(qr, r, p, pos, a.log2_base);
+            rope_pair(qr, r, cs[p][0], cs[p][1]);
             qr[0] = r[0];
             qr[1] = r[1];
         } else {
