@@ -131,6 +131,19 @@ def measure_extras(mla, case, dev, q, cache, bt, sl, steps: int):
     except Exception as exc:   # the timing stands without the check
         rec["parity_sampled_tokens"] = f"skipped: {exc}"
     out["sparse_topk2048"] = rec
+    from mla_decode_attention_amd.inputs import make_absorb_inputs
+    qn, qr, wuk, wuv = (torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+                        for x in make_absorb_inputs(b, s_q, h, seed=9))
+    qa = torch.empty((b, s_q, h, 576), dtype=torch.bfloat16, device=dev)
+    ol = torch.randn((b, s_q, h, 512), device=dev).to(torch.bfloat16)
+    oo = torch.empty((b, s_q, h, 128), dtype=torch.bfloat16, device=dev)
+    us_a = timed(lambda: mla.absorb_q(qn, qr, wuk, qa))
+    us_u = timed(lambda: mla.unabsorb_o(ol, wuv, oo))
+    wbytes = h * 512 * 128 * 2
+    out["absorb_q"] = {"us": round(us_a, 2), "weight_bytes": wbytes, "GB/s": round(wbytes / us_a / 1e3, 1),
+                       "bound": "launch / HBM (weights)"}
+    out["unabsorb_o"] = {"us": round(us_u, 2), "weight_bytes": wbytes, "GB/s": round(wbytes / us_u / 1e3, 1),
+                         "bound": "launch / HBM (weights)"}
     # the append writes the new tokens' rows into the cache: measured after the sparse check
     lat, rope = make_append_inputs(case, seed=7)
     lat_d = torch.from_numpy(lat.view(np.int16)).to(dev).view(torch.bfloat16)

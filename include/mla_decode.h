@@ -130,6 +130,34 @@ int mla_decode_fwd_combine(const int32_t *seqlens, int bt_stride, int batch, int
                            float *lse, void *stream);
 
 /*
+ * Absorption and un-absorption around the decode path: the up-projections are absorbed into the
+ * query and output projections so every head attends the latent cache directly (GQLA summary,
+ * section "Arquitetura", item 1).  The per-head no-RoPE width is 128 (MLA_DECODE_D_NOPE, a
+ * reading: the pages give only the latent and RoPE widths).  Per head h and query token
+ * m = b * s_q + i, in fp32 from bf16 inputs, outputs rounded once to bf16 (nearest even):
+ *   mla_absorb_q:    q[m][h][0:512] = W_UK[h] q_nope[m][h],  q[m][h][512:576] = q_rope[m][h]
+ *   mla_unabsorb_o:  o[m][h][0:128] = W_UV[h] o_latent[m][h]
+ * so that attention of the absorbed query over the latent cache followed by the un-absorption
+ * equals attention with per-head keys W_UK[h]^T c_j (plus the RoPE key) and values W_UV[h] c_j.
+ *   q_nope    bf16 [batch][s_q][num_heads][128], device, 16-B aligned
+ *   q_rope    bf16 [batch][s_q][num_heads][64], device, 16-B aligned
+ *   w_uk      bf16 [num_heads][512][128], device: row n of W_UK[h] holds the 128 no-RoPE weights of
+ *             latent dim n
+ *   q         bf16 [batch][s_q][num_heads][576], device, written (the decode path's query)
+ *   o_latent  bf16 [batch][s_q][num_heads][512], device (the decode path's output)
+ *   w_uv      bf16 [num_heads][128][512], device: row d of W_UV[h] maps the latent to output dim d
+ *   o         bf16 [batch][s_q][num_heads][128], device, written
+ * num_heads and s_q as for mla_decode_fwd.  Returns MLA_OK or an error code (nothing launched).
+ */
+#define MLA_DECODE_D_NOPE 128
+
+int mla_absorb_q(const void *q_nope, const void *q_rope, const void *w_uk, int batch, int s_q,
+                 int num_heads, void *q, void *stream);
+
+int mla_unabsorb_o(const void *o_latent, const void *w_uv, int batch, int s_q, int num_heads,
+                   void *o, void *stream);
+
+/*
  * Sparse (top-k) decode: every head of query token (b, i) attends exactly the cache rows that
  * token's index list names instead of all L_b rows (GQLA summary, section "GQLA Esparso":
  * fine-grained sparse attention over the latent cache; how the rows are selected is an input).

@@ -15,6 +15,8 @@ Names follow the C ABI:
   * :func:`fwd_combine`    -> ``mla_decode_fwd_combine`` (second half of fwd)
   * :func:`status_string`  -> ``mla_decode_status_string``
   * :func:`cache_append_rope` -> ``mla_cache_append_rope`` (new tokens into the paged cache)
+  * :func:`absorb_q`, :func:`unabsorb_o` -> ``mla_absorb_q`` / ``mla_unabsorb_o`` (per-head
+    projections into and out of the latent space, either side of the decode path)
   * :func:`sparse_workspace_size`, :func:`sparse_plan`, :func:`sparse_fwd` ->
     ``mla_sparse_decode_workspace_size`` / ``_plan`` / ``_fwd`` (top-k decode)
 plus :func:`decode`, which allocates the workspace/outputs and calls plan + fwd.
@@ -36,7 +38,9 @@ STATUS = {0: "MLA_OK", -1: "MLA_ERR_INVALID_ARG", -2: "MLA_ERR_UNSUPPORTED",
           -3: "MLA_ERR_WORKSPACE_TOO_SMALL", -4: "MLA_ERR_NO_DEVICE", -5: "MLA_ERR_HIP"}
 EXPORTS = ("mla_decode_workspace_size", "mla_decode_plan", "mla_decode_fwd", "mla_decode_fwd_split",
            "mla_decode_fwd_combine", "mla_decode_status_string", "mla_cache_append_rope",
-           "mla_sparse_decode_workspace_size", "mla_sparse_decode_plan", "mla_sparse_decode_fwd")
+           "mla_sparse_decode_workspace_size", "mla_sparse_decode_plan", "mla_sparse_decode_fwd",
+           "mla_absorb_q", "mla_unabsorb_o")
+D_NOPE = 128
 
 
 class MlaDecodeError(RuntimeError):
@@ -73,6 +77,10 @@ def lib() -> ctypes.CDLL:
     L.mla_sparse_decode_plan.restype = I
     L.mla_sparse_decode_fwd.argtypes = [P, P, P, I, P, P, I, I, I, I, I, I, ctypes.c_float, P, SZ, P, P, P]
     L.mla_sparse_decode_fwd.restype = I
+    L.mla_absorb_q.argtypes = [P, P, P, I, I, I, P, P]
+    L.mla_absorb_q.restype = I
+    L.mla_unabsorb_o.argtypes = [P, P, I, I, I, P, P]
+    L.mla_unabsorb_o.restype = I
     L.mla_decode_status_string.argtypes = [I]
     L.mla_decode_status_string.restype = ctypes.c_char_p
     _LIB = L
@@ -208,6 +216,47 @@ def cache_append_rope(kv_latent, k_rope, q, kv_cache, block_table, seqlens, rope
         kv_latent.data_ptr(), k_rope.data_ptr(), q.data_ptr(), kv_cache.data_ptr(), block_table.data_ptr(),
         block_table.shape[1], seqlens.data_ptr(), b, s_q, h, kv_cache.shape[0], kv_cache.shape[1], float(rope_base),
         _stream(stream)))
+
+
+def absorb_q(q_nope, q_rope, w_uk, q=None, stream=None):
+    """mla_absorb_q: the decode path's query [b, s_q, h, 576] from q_nope [b, s_q, h, 128], q_rope
+    [b, s_q, h, 64] and W_UK [h, 512, 128]; allocates ``q`` if not given."""
+    import torch
+    _require(q_nope, "q_nope", torch.bfloat16, 4)
+    dev = q_nope.device
+    _require(q_rope, "q_rope", torch.bfloat16, 4, dev)
+    _require(w_uk, "w_uk", torch.bfloat16, 3, dev)
+    b, s_q, h, dn = q_nope.shape
+    if dn != D_NOPE or tuple(q_rope.shape) != (b, s_q, h, D_K - D_V) or tuple(w_uk.shape) != (h, D_V, D_NOPE):
+        raise ValueError("q_nope [b, s_q, h, 128], q_rope [b, s_q, h, 64], w_uk [h, 512, 128]")
+    if q is None:
+        q = torch.empty((b, s_q, h, D_K), dtype=torch.bfloat16, device=dev)
+    _require(q, "q", torch.bfloat16, 4, dev)
+    if tuple(q.shape) != (b, s_q, h, D_K):
+        raise ValueError("q must be [b, s_q, h, 576]")
+    _check("mla_absorb_q", lib().mla_absorb_q(q_nope.data_ptr(), q_rope.data_ptr(), w_uk.data_ptr(), b, s_q, h,
+                                              q.data_ptr(), _stream(stream)))
+    return q
+
+
+def unabsorb_o(o_latent, w_uv, o=None, stream=None):
+    """mla_unabsorb_o: per-head output [b, s_q, h, 128] from the decode output [b, s_q, h, 512] and
+    W_UV [h, 128, 512]; allocates ``o`` if not given."""
+    import torch
+    _require(o_latent, "o_latent", torch.bfloat16, 4)
+    dev = o_latent.device
+    _require(w_uv, "w_uv", torch.bfloat16, 3, dev)
+    b, s_q, h, dl = o_latent.shape
+    if dl != D_V or tuple(w_uv.shape) != (h, D_NOPE, D_V):
+        raise ValueError("o_latent [b, s_q, h, 512], w_uv [h, 128, 512]")
+    if o is None:
+        o = torch.empty((b, s_q, h, D_NOPE), dtype=torch.bfloat16, device=dev)
+    _require(o, "o", torch.bfloat16, 4, dev)
+    if tuple(o.shape) != (b, s_q, h, D_NOPE):
+        raise ValueError("o must be [b, s_q, h, 128]")
+    _check("mla_unabsorb_o", lib().mla_unabsorb_o(o_latent.data_ptr(), w_uv.data_ptr(), b, s_q, h, o.data_ptr(),
+                                                  _stream(stream)))
+    return o
 
 
 def sparse_workspace_size(batch: int, s_q: int, num_heads: int, topk: int) -> int:

@@ -9,6 +9,7 @@
 #include <cstring>
 #include <mutex>
 
+#include "mla_absorb_kernels.h"
 #include "mla_append_kernels.h"
 #include "mla_decode_kernels.h"
 
@@ -407,6 +408,76 @@ int mla_sparse_decode_fwd(const void* q, const void* kv_cache, const int32_t* bl
     c.seqlens = reinterpret_cast<const int32_t*>(a.ws + lay.seqlens);
     c.bt_stride = (topk + kPage - 1) / kPage;
     return launch_combine(c, s);
+}
+
+namespace {
+
+int launch_head_gemm(const HeadGemmArgs& g, int heads, hipStream_t s)
+{
+    hipLaunchKernelGGL(head_gemm_kernel, dim3(heads, g.N / 64, (g.M + 15) / 16), dim3(kAbsorbThreads), 0, s, g);
+    return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int absorb_shape_ok(int batch, int s_q, int num_heads)
+{
+    if (batch < 1 || (long long)batch * s_q > (1 << 20)) return MLA_ERR_INVALID_ARG;
+    return heads_ok(s_q, num_heads) ? MLA_OK : MLA_ERR_UNSUPPORTED;
+}
+
+}  // namespace
+
+int mla_absorb_q(const void* q_nope, const void* q_rope, const void* w_uk, int batch, int s_q, int num_heads,
+                 void* q, void* stream)
+{
+    if (!q_nope || !q_rope || !w_uk || !q) return MLA_ERR_INVALID_ARG;
+    if (!aligned(q_nope, 16) || !aligned(q_rope, 16) || !aligned(w_uk, 16) || !aligned(q, 16))
+        return MLA_ERR_INVALID_ARG;
+    int st = absorb_shape_ok(batch, s_q, num_heads);
+    if (st != MLA_OK) return st;
+    const DeviceInfo* d = nullptr;
+    st = device_info(&d);
+    if (st != MLA_OK) return st;
+    HeadGemmArgs g{};
+    g.a = static_cast<const uint16_t*>(q_nope);
+    g.w = static_cast<const uint16_t*>(w_uk);
+    g.c = static_cast<uint16_t*>(q);
+    g.lda = (long long)num_heads * kDNope;
+    g.a_head = kDNope;
+    g.w_head = (long long)kDv * kDNope;
+    g.ldc = (long long)num_heads * kDk;
+    g.c_head = kDk;
+    g.M = batch * s_q;
+    g.N = kDv;
+    g.K = kDNope;
+    g.rope = static_cast<const uint16_t*>(q_rope);
+    g.heads = num_heads;
+    return launch_head_gemm(g, num_heads, static_cast<hipStream_t>(stream));
+}
+
+int mla_unabsorb_o(const void* o_latent, const void* w_uv, int batch, int s_q, int num_heads, void* o, void* stream)
+{
+    if (!o_latent || !w_uv || !o) return MLA_ERR_INVALID_ARG;
+    if (!aligned(o_latent, 16) || !aligned(w_uv, 16) || !aligned(o, 2)) return MLA_ERR_INVALID_ARG;
+    int st = absorb_shape_ok(batch, s_q, num_heads);
+    if (st != MLA_OK) return st;
+    const DeviceInfo* d = nullptr;
+    st = device_info(&d);
+    if (st != MLA_OK) return st;
+    HeadGemmArgs g{};
+    g.a = static_cast<const uint16_t*>(o_latent);
+    g.w = static_cast<const uint16_t*>(w_uv);
+    g.c = static_cast<uint16_t*>(o);
+    g.lda = (long long)num_heads * kDv;
+    g.a_head = kDv;
+    g.w_head = (long long)kDNope * kDv;
+    g.ldc = (long long)num_heads * kDNope;
+    g.c_head = kDNope;
+    g.M = batch * s_q;
+    g.N = kDNope;
+    g.K = kDv;
+    g.rope = nullptr;
+    g.heads = num_heads;
+    return launch_head_gemm(g, num_heads, static_cast<hipStream_t>(stream));
 }
 
 const char* mla_decode_status_string(int status)

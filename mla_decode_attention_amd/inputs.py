@@ -189,3 +189,14 @@ def make_sparse_indices(case: DecodeCase, topk: int, seed: int, *, pad_frac: flo
                 row[rng.random(topk) < pad_frac] = -1
             out[b, i] = rng.permutation(row)
     return out
+
+
+def make_absorb_inputs(batch: int, s_q: int, heads: int, seed: int):
+    """Seeded bf16 bit arrays for the absorption steps: q_nope [b, s_q, h, 128], q_rope [b, s_q, h, 64]
+    ~ N(0, 1), and random per-head weights W_UK [h, 512, 128], W_UV [h, 128, 512] ~ N(0, 1/256)."""
+    rng = np.random.default_rng(seed)
+    qn = rng.standard_normal((batch, s_q, heads, 128), dtype=np.float32)
+    qr = rng.standard_normal((batch, s_q, heads, D_K - D_V), dtype=np.float32)
+    wuk = rng.standard_normal((heads, D_V, 128), dtype=np.float32) / 16
+    wuv = rng.standard_normal((heads, 128, D_V), dtype=np.float32) / 16
+    return f32_to_bf16_bits(qn), f32_to_bf16_bits(qr), f32_to_bf16_bits(wuk), f32_to_bf16_bits(wuv)

@@ -143,6 +143,18 @@ def test_sparse_plan_and_size_argument_errors(L):
     assert L.mla_sparse_decode_plan(1, 3, 16, 64, P(FAKE), 1 << 20, None) == -2
 
 
+def test_absorb_argument_errors(L):
+    f = P(FAKE)
+    assert L.mla_absorb_q(None, f, f, 1, 1, 16, f, None) == -1
+    assert L.mla_absorb_q(f, f, f, 0, 1, 16, f, None) == -1
+    assert L.mla_absorb_q(P(FAKE + 8), f, f, 1, 1, 16, f, None) == -1
+    assert L.mla_absorb_q(f, f, f, 1, 1, 24, f, None) == -2
+    assert L.mla_absorb_q(f, f, f, 1, 3, 16, f, None) == -2
+    assert L.mla_unabsorb_o(f, None, 1, 1, 16, f, None) == -1
+    assert L.mla_unabsorb_o(f, f, 0, 1, 16, f, None) == -1
+    assert L.mla_unabsorb_o(f, f, 1, 2, 256, f, None) == -2
+
+
 def test_valid_arguments_without_a_gpu_report_no_device(L):
     import torch
     if torch.cuda.is_available():
@@ -153,6 +165,8 @@ def test_valid_arguments_without_a_gpu_report_no_device(L):
     assert _fwd(L) == -4
     assert _append(L) == -4
     assert _sparse_fwd(L) == -4
+    assert L.mla_absorb_q(P(FAKE), P(FAKE), P(FAKE), 1, 1, 16, P(FAKE), None) == -4
+    assert L.mla_unabsorb_o(P(FAKE), P(FAKE), 1, 1, 16, P(FAKE), None) == -4
     assert L.mla_sparse_decode_plan(1, 1, 16, 64, P(FAKE), 1 << 20, None) == -4
     with pytest.raises(mla.MlaDecodeError):
         mla.workspace_size(16, 1, 16)
