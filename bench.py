@@ -144,6 +144,52 @@ def measure_extras(mla, case, dev, q, cache, bt, sl, steps: int):
                        "bound": "launch / HBM (weights)"}
     out["unabsorb_o"] = {"us": round(us_u, 2), "weight_bytes": wbytes, "GB/s": round(wbytes / us_u / 1e3, 1),
                          "bound": "launch / HBM (weights)"}
+    # GQA path of GQLA on the MTP-shaped workload (one group: 16 heads, two causal query tokens,
+    # L ~ U{8192..16384}), beside the absorbed path on the same lengths
+    from mla_decode_attention_amd import workloads as W
+    from mla_decode_attention_amd.inputs import make_case as _mk
+    spec = dict(W.WORKLOADS["mtp_b16_h16_sq2_L8K-16K"])
+    spec.pop("outlier_frac", None)
+    spec.pop("outlier_scale", None)
+    gcase = _mk("gqa_b16_sq2_L8K-16K", row_dims=320, q_dims=192, **spec)
+    gq = torch.from_numpy(gcase.q.view(np.int16)).to(dev).view(torch.bfloat16)
+    gc = torch.from_numpy(gcase.cache.view(np.int16)).to(dev).view(torch.bfloat16)
+    gbt = torch.from_numpy(gcase.block_table).to(dev)
+    gsl = torch.from_numpy(gcase.seqlens).to(dev)
+    gws = torch.empty(mla.gqa_workspace_size(gcase.batch, 2, 16), dtype=torch.uint8, device=dev)
+    go = torch.empty((gcase.batch, 2, 16, 128), dtype=torch.bfloat16, device=dev)
+    gl = torch.empty((gcase.batch, 2, 16), dtype=torch.float32, device=dev)
+    mla.gqa_plan(gsl, 2, 16, gws)
+    us_g = timed(lambda: mla.gqa_fwd(gq, gc, gbt, gsl, gcase.softmax_scale, True, gws, go, gl))
+    gbytes = int(gcase.seqlens.astype(np.int64).sum()) * 640 + gcase.batch * 2 * 16 * 192 * 2
+    grec = {"us": round(us_g, 2), "bytes": gbytes, "GB/s": round(gbytes / us_g / 1e3, 1),
+            "frac_of_hbm_peak": round(gbytes / us_g / 1e3 / HBM_PEAK_GBS, 4), "bound": "hbm",
+            "config": "b16 s_q2 causal, 16 heads of one group, d_h 128, L ~ U{8192..16384}"}
+    try:
+        import oracle.gqa as OG
+        from mla_decode_attention_amd.inputs import bf16_bits_to_f32
+        og = bf16_bits_to_f32(go.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+        sel = [0, gcase.batch - 1]
+        ro, rl = OG.gqa_decode(gcase.q[sel], gcase.cache, gcase.block_table[sel], gcase.seqlens[sel],
+                               gcase.softmax_scale, True)
+        grec["parity_sampled_sequences"] = {"sequences": 2, "o_maxabs": float(np.abs(og[sel] - ro).max())}
+    except Exception as exc:
+        grec["parity_sampled_sequences"] = f"skipped: {exc}"
+    out["gqa_mtp_b16_sq2_L8K-16K"] = grec
+    del gq, gc, gws
+    mcase = W.build("mtp_b16_h16_sq2_L8K-16K")
+    mq = torch.from_numpy(mcase.q.view(np.int16)).to(dev).view(torch.bfloat16)
+    mc = torch.from_numpy(mcase.cache.view(np.int16)).to(dev).view(torch.bfloat16)
+    mbt = torch.from_numpy(mcase.block_table).to(dev)
+    msl = torch.from_numpy(mcase.seqlens).to(dev)
+    mws = torch.empty(mla.workspace_size(mcase.batch, 2, 16), dtype=torch.uint8, device=dev)
+    mo = torch.empty((mcase.batch, 2, 16, 512), dtype=torch.bfloat16, device=dev)
+    ml_ = torch.empty((mcase.batch, 2, 16), dtype=torch.float32, device=dev)
+    mla.plan(msl, 2, 16, mws)
+    us_m = timed(lambda: mla.fwd(mq, mc, mbt, msl, mcase.softmax_scale, True, mws, mo, ml_))
+    mbytes = int(mcase.seqlens.astype(np.int64).sum()) * 1152 + mcase.batch * 2 * 16 * 576 * 2
+    out["mla_absorbed_same_lengths"] = {"us": round(us_m, 2), "bytes": mbytes, "GB/s": round(mbytes / us_m / 1e3, 1)}
+    del mq, mc, mws
     # the append writes the new tokens' rows into the cache: measured after the sparse check
     lat, rope = make_append_inputs(case, seed=7)
     lat_d = torch.from_numpy(lat.view(np.int16)).to(dev).view(torch.bfloat16)

@@ -130,6 +130,35 @@ int mla_decode_fwd_combine(const int32_t *seqlens, int bt_stride, int batch, int
                            float *lse, void *stream);
 
 /*
+ * GQA-path decode of GQLA: the latent expanded into g groups of keys and values, decoded as
+ * standard grouped-query attention over a cache holding the group's keys and values plus the
+ * shared RoPE key (GQLA summary, section "Arquitetura", item 2).  One GPU's share is one group:
+ * 16 query heads (h_q / g = 16).  Readings (the pages give neither): per-group width d_h = 128
+ * (MLA_GQA_D_H); one cache row per token, [k (128) | shared RoPE key (64) | v (128)]
+ * (MLA_GQA_ROW = 320 bf16).  For sequence b, query token i, head h and visible rows j (as for
+ * mla_decode_fwd, bottom-right causal when causal != 0):
+ *     s_j = softmax_scale * dot(q[b,i,h,0:192], row_j[0:192]),  LSE = ln sum_j exp(s_j),
+ *     O   = sum_j exp(s_j - LSE) * row_j[192:320].
+ *   q         bf16 [batch][s_q][16][192]: [q_nope (128) | q_rope (64)] of the group's heads
+ *   kv_cache  bf16 [num_pages][64][320], paged as for mla_decode_fwd
+ *   out       bf16 [batch][s_q][16][128]; lse fp32 [batch][s_q][16]
+ *   num_heads must be 16, s_q 1 or 2; the other arguments, the plan/workspace protocol and the
+ *   device-side error rules are those of mla_decode_plan / mla_decode_fwd.
+ */
+#define MLA_GQA_D_H 128
+#define MLA_GQA_ROW 320
+
+int mla_gqa_decode_workspace_size(int batch, int s_q, int num_heads, size_t *bytes);
+
+int mla_gqa_decode_plan(const int32_t *seqlens, int batch, int s_q, int num_heads, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
+int mla_gqa_decode_fwd(const void *q, const void *kv_cache, const int32_t *block_table, int bt_stride,
+                       const int32_t *seqlens, int batch, int s_q, int num_heads, int num_pages,
+                       int page_size, float softmax_scale, int causal, void *workspace,
+                       size_t workspace_bytes, void *out, float *lse, void *stream);
+
+/*
  * Absorption and un-absorption around the decode path: the up-projections are absorbed into the
  * query and output projections so every head attends the latent cache directly (GQLA summary,
  * section "Arquitetura", item 1).  The per-head no-RoPE width is 128 (MLA_DECODE_D_NOPE, a

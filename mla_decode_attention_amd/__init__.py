@@ -15,6 +15,8 @@ Names follow the C ABI:
   * :func:`fwd_combine`    -> ``mla_decode_fwd_combine`` (second half of fwd)
   * :func:`status_string`  -> ``mla_decode_status_string``
   * :func:`cache_append_rope` -> ``mla_cache_append_rope`` (new tokens into the paged cache)
+  * :func:`gqa_workspace_size`, :func:`gqa_plan`, :func:`gqa_fwd` -> ``mla_gqa_decode_*`` (the
+    GQA path of GQLA: one group's 16 heads over its expanded key/value cache)
   * :func:`absorb_q`, :func:`unabsorb_o` -> ``mla_absorb_q`` / ``mla_unabsorb_o`` (per-head
     projections into and out of the latent space, either side of the decode path)
   * :func:`sparse_workspace_size`, :func:`sparse_plan`, :func:`sparse_fwd` ->
@@ -39,7 +41,10 @@ STATUS = {0: "MLA_OK", -1: "MLA_ERR_INVALID_ARG", -2: "MLA_ERR_UNSUPPORTED",
 EXPORTS = ("mla_decode_workspace_size", "mla_decode_plan", "mla_decode_fwd", "mla_decode_fwd_split",
            "mla_decode_fwd_combine", "mla_decode_status_string", "mla_cache_append_rope",
            "mla_sparse_decode_workspace_size", "mla_sparse_decode_plan", "mla_sparse_decode_fwd",
-           "mla_absorb_q", "mla_unabsorb_o")
+           "mla_absorb_q", "mla_unabsorb_o", "mla_gqa_decode_workspace_size", "mla_gqa_decode_plan",
+           "mla_gqa_decode_fwd")
+GQA_D_H = 128
+GQA_ROW = 320
 D_NOPE = 128
 
 
@@ -81,6 +86,12 @@ def lib() -> ctypes.CDLL:
     L.mla_absorb_q.restype = I
     L.mla_unabsorb_o.argtypes = [P, P, I, I, I, P, P]
     L.mla_unabsorb_o.restype = I
+    L.mla_gqa_decode_workspace_size.argtypes = [I, I, I, ctypes.POINTER(SZ)]
+    L.mla_gqa_decode_workspace_size.restype = I
+    L.mla_gqa_decode_plan.argtypes = [P, I, I, I, P, SZ, P]
+    L.mla_gqa_decode_plan.restype = I
+    L.mla_gqa_decode_fwd.argtypes = [P, P, P, I, P, I, I, I, I, I, ctypes.c_float, I, P, SZ, P, P, P]
+    L.mla_gqa_decode_fwd.restype = I
     L.mla_decode_status_string.argtypes = [I]
     L.mla_decode_status_string.restype = ctypes.c_char_p
     _LIB = L
@@ -216,6 +227,57 @@ def cache_append_rope(kv_latent, k_rope, q, kv_cache, block_table, seqlens, rope
         kv_latent.data_ptr(), k_rope.data_ptr(), q.data_ptr(), kv_cache.data_ptr(), block_table.data_ptr(),
         block_table.shape[1], seqlens.data_ptr(), b, s_q, h, kv_cache.shape[0], kv_cache.shape[1], float(rope_base),
         _stream(stream)))
+
+
+def gqa_workspace_size(batch: int, s_q: int, num_heads: int = 16) -> int:
+    out = ctypes.c_size_t(0)
+    _check("mla_gqa_decode_workspace_size",
+           lib().mla_gqa_decode_workspace_size(int(batch), int(s_q), int(num_heads), ctypes.byref(out)))
+    return int(out.value)
+
+
+def gqa_plan(seqlens, s_q: int, num_heads: int, workspace, stream=None) -> None:
+    import torch
+    _require(seqlens, "seqlens", torch.int32, 1)
+    _require(workspace, "workspace", torch.uint8, 1, seqlens.device)
+    _check("mla_gqa_decode_plan", lib().mla_gqa_decode_plan(seqlens.data_ptr(), seqlens.shape[0], int(s_q),
+                                                            int(num_heads), workspace.data_ptr(), workspace.numel(),
+                                                            _stream(stream)))
+
+
+def gqa_fwd(q, kv_cache, block_table, seqlens, softmax_scale: float, causal: bool, workspace, out, lse,
+            stream=None) -> None:
+    """mla_gqa_decode_fwd: O bf16 [b, s_q, 16, 128] and LSE [b, s_q, 16] over the group's cache [pages, 64, 320]."""
+    import torch
+    _require(q, "q", torch.bfloat16, 4)
+    dev = q.device
+    _require(kv_cache, "kv_cache", torch.bfloat16, 3, dev)
+    _require(block_table, "block_table", torch.int32, 2, dev)
+    _require(seqlens, "seqlens", torch.int32, 1, dev)
+    _require(workspace, "workspace", torch.uint8, 1, dev)
+    _require(out, "out", torch.bfloat16, 4, dev)
+    _require(lse, "lse", torch.float32, 3, dev)
+    b, s_q, h, dk = q.shape
+    if dk != GQA_D_H + 64 or kv_cache.shape[2] != GQA_ROW:
+        raise ValueError("q rows must be 192 wide and cache rows 320 wide")
+    if tuple(out.shape) != (b, s_q, h, GQA_D_H) or tuple(lse.shape) != (b, s_q, h):
+        raise ValueError("out must be [b, s_q, h, 128] and lse [b, s_q, h]")
+    _check("mla_gqa_decode_fwd", lib().mla_gqa_decode_fwd(
+        q.data_ptr(), kv_cache.data_ptr(), block_table.data_ptr(), block_table.shape[1], seqlens.data_ptr(), b, s_q, h,
+        kv_cache.shape[0], kv_cache.shape[1], float(softmax_scale), int(bool(causal)), workspace.data_ptr(),
+        workspace.numel(), out.data_ptr(), lse.data_ptr(), _stream(stream)))
+
+
+def gqa_decode(q, kv_cache, block_table, seqlens, softmax_scale: float, causal: bool = False, stream=None):
+    """Allocate the workspace and outputs, plan and run one GQA-path decode step."""
+    import torch
+    b, s_q, h, _ = q.shape
+    ws = torch.empty(gqa_workspace_size(b, s_q, h), dtype=torch.uint8, device=q.device)
+    out = torch.empty((b, s_q, h, GQA_D_H), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((b, s_q, h), dtype=torch.float32, device=q.device)
+    gqa_plan(seqlens, s_q, h, ws, stream)
+    gqa_fwd(q, kv_cache, block_table, seqlens, softmax_scale, causal, ws, out, lse, stream)
+    return out, lse
 
 
 def absorb_q(q_nope, q_rope, w_uk, q=None, stream=None):

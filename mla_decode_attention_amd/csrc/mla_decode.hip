@@ -11,6 +11,7 @@
 
 #include "mla_absorb_kernels.h"
 #include "mla_append_kernels.h"
+#include "mla_gqa_kernels.h"
 #include "mla_decode_kernels.h"
 
 namespace {
@@ -27,7 +28,11 @@ using CfgR16 = SplitCfg<4, 1, 1, 16, 1, 1>;    // 4 independent waves, one 18 Ki
 using CfgW32 = WideCfg<1, 5, 2>;               // 32 rows per workgroup
 using CfgW64 = WideCfg<1, 5, 4>;               // 64 rows per workgroup (row groups of 64 above)
 
-enum CfgId { kR16 = 0, kW32, kW64, kS16, kNumCfg };   // kS16: sparse (gathered-row) form of kR16
+using CfgG1 = GqaCfg<1>;                       // GQA path, one query token per step
+using CfgG2 = GqaCfg<2>;                       // GQA path, two query tokens per step
+
+// kS16: sparse (gathered-row) form of kR16; kG1 / kG2: GQA path
+enum CfgId { kR16 = 0, kW32, kW64, kS16, kG1, kG2, kNumCfg };
 
 struct LaunchGeom {
     CfgId cfg;
@@ -55,6 +60,8 @@ const void* split_fn(CfgId c)
     case kR16: return reinterpret_cast<const void*>(&split_kernel<CfgR16>);
     case kW32: return reinterpret_cast<const void*>(&split_wide_kernel<CfgW32>);
     case kS16: return reinterpret_cast<const void*>(&split_kernel<CfgR16, true>);
+    case kG1: return reinterpret_cast<const void*>(&gqa_split_kernel<CfgG1>);
+    case kG2: return reinterpret_cast<const void*>(&gqa_split_kernel<CfgG2>);
     default: return reinterpret_cast<const void*>(&split_wide_kernel<CfgW64>);
     }
 }
@@ -94,9 +101,10 @@ int device_info(const DeviceInfo** out)
             d.status = MLA_ERR_NO_DEVICE;   // the code objects are built for gfx950 only
         } else {
             d.num_cu = prop.multiProcessorCount;
-            static const int threads[kNumCfg] = {CfgR16::THREADS, CfgW32::THREADS, CfgW64::THREADS, CfgR16::THREADS};
+            static const int threads[kNumCfg] = {CfgR16::THREADS, CfgW32::THREADS, CfgW64::THREADS,
+                                                 CfgR16::THREADS, kGqaThreads,     kGqaThreads};
             static const int lds[kNumCfg] = {CfgR16::LDS_BYTES, CfgW32::LDS_BYTES, CfgW64::LDS_BYTES,
-                                             CfgR16::LDS_BYTES};
+                                             CfgR16::LDS_BYTES, CfgG1::LDS_BYTES, CfgG2::LDS_BYTES};
             for (int c = 0; c < kNumCfg; ++c) {
                 const void* fn = split_fn(static_cast<CfgId>(c));
                 int occ = 0;
@@ -233,7 +241,7 @@ int launch_split(const FwdArgs& a, const LaunchGeom& g, hipStream_t s)
 
 int launch_combine(const FwdArgs& a, hipStream_t s)
 {
-    hipLaunchKernelGGL(combine_kernel, dim3(a.batch * a.rows), dim3(kCombineThreads), 0, s, a);
+    hipLaunchKernelGGL(combine_kernel_t<kDv>, dim3(a.batch * a.rows), dim3(kCombineThreads), 0, s, a);
     return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -478,6 +486,98 @@ int mla_unabsorb_o(const void* o_latent, const void* w_uv, int batch, int s_q, i
     g.rope = nullptr;
     g.heads = num_heads;
     return launch_head_gemm(g, num_heads, static_cast<hipStream_t>(stream));
+}
+
+namespace {
+
+int gqa_geom(int batch, int s_q, int num_heads, LaunchGeom* g)
+{
+    if (batch < 1) return MLA_ERR_INVALID_ARG;
+    if ((s_q != 1 && s_q != 2) || num_heads != kGqaHeads) return MLA_ERR_UNSUPPORTED;
+    *g = s_q == 1 ? LaunchGeom{kG1, 1, kGqaThreads, CfgG1::LDS_BYTES} : LaunchGeom{kG2, 1, kGqaThreads, CfgG2::LDS_BYTES};
+    return MLA_OK;
+}
+
+}  // namespace
+
+int mla_gqa_decode_workspace_size(int batch, int s_q, int num_heads, size_t* bytes)
+{
+    if (!bytes) return MLA_ERR_INVALID_ARG;
+    LaunchGeom g;
+    int st = gqa_geom(batch, s_q, num_heads, &g);
+    if (st != MLA_OK) return st;
+    const DeviceInfo* d = nullptr;
+    st = device_info(&d);
+    if (st != MLA_OK) return st;
+    *bytes = ws_layout(batch, s_q * num_heads, item_capacity(*d, g, batch), kGqaDv).total;
+    return MLA_OK;
+}
+
+int mla_gqa_decode_plan(const int32_t* seqlens, int batch, int s_q, int num_heads, void* workspace,
+                        size_t workspace_bytes, void* stream)
+{
+    if (!seqlens || !workspace || !aligned(workspace, 256) || !aligned(seqlens, 4)) return MLA_ERR_INVALID_ARG;
+    LaunchGeom g;
+    int st = gqa_geom(batch, s_q, num_heads, &g);
+    if (st != MLA_OK) return st;
+    const DeviceInfo* d = nullptr;
+    st = device_info(&d);
+    if (st != MLA_OK) return st;
+    const int rows = s_q * num_heads;
+    const int cap = item_capacity(*d, g, batch);
+    if (workspace_bytes < ws_layout(batch, rows, cap, kGqaDv).total) return MLA_ERR_WORKSPACE_TOO_SMALL;
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, static_cast<hipStream_t>(stream), seqlens, batch,
+                       s_q, num_heads, rows, gx_of(*d, g), cap, static_cast<char*>(workspace), -1);
+    return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int mla_gqa_decode_fwd(const void* q, const void* kv_cache, const int32_t* block_table, int bt_stride,
+                       const int32_t* seqlens, int batch, int s_q, int num_heads, int num_pages, int page_size,
+                       float softmax_scale, int causal, void* workspace, size_t workspace_bytes, void* out, float* lse,
+                       void* stream)
+{
+    if (!q || !kv_cache || !block_table || !seqlens || !workspace || !out || !lse) return MLA_ERR_INVALID_ARG;
+    if (bt_stride < 1 || num_pages < 1 || !std::isfinite(softmax_scale) || (causal != 0 && causal != 1))
+        return MLA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(block_table, 4) || !aligned(seqlens, 4) ||
+        !aligned(workspace, 256) || !aligned(out, 2) || !aligned(lse, 4))
+        return MLA_ERR_INVALID_ARG;
+    LaunchGeom g;
+    int st = gqa_geom(batch, s_q, num_heads, &g);
+    if (st != MLA_OK) return st;
+    if (page_size != MLA_DECODE_PAGE_SIZE) return MLA_ERR_UNSUPPORTED;
+    const DeviceInfo* d = nullptr;
+    st = device_info(&d);
+    if (st != MLA_OK) return st;
+    const int rows = s_q * num_heads;
+    const int cap = item_capacity(*d, g, batch);
+    if (workspace_bytes < ws_layout(batch, rows, cap, kGqaDv).total) return MLA_ERR_WORKSPACE_TOO_SMALL;
+    FwdArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.cache = static_cast<const uint16_t*>(kv_cache);
+    a.block_table = block_table;
+    a.seqlens = seqlens;
+    a.ws = static_cast<char*>(workspace);
+    a.out = static_cast<uint16_t*>(out);
+    a.lse = lse;
+    a.num_pages = num_pages;
+    a.bt_stride = bt_stride;
+    a.batch = batch;
+    a.s_q = s_q;
+    a.heads = num_heads;
+    a.rows = rows;
+    a.capacity = cap;
+    a.scale_log2 = softmax_scale * kLog2e;
+    a.causal = causal;
+    a.row_groups = 1;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (s_q == 1)
+        hipLaunchKernelGGL(gqa_split_kernel<CfgG1>, dim3(cap), dim3(kGqaThreads), CfgG1::LDS_BYTES, s, a);
+    else
+        hipLaunchKernelGGL(gqa_split_kernel<CfgG2>, dim3(cap), dim3(kGqaThreads), CfgG2::LDS_BYTES, s, a);
+    if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
+    hipLaunchKernelGGL(combine_kernel_t<kGqaDv>, dim3(batch * rows), dim3(kCombineThreads), 0, s, a);
+    return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
 const char* mla_decode_status_string(int status)

@@ -20,6 +20,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace mla {
 
 constexpr int kDk = 576;
@@ -58,7 +60,8 @@ struct WsLayout {
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-__host__ __device__ inline WsLayout ws_layout(int batch, int rows, int capacity)
+// dv: width of a partial output row (512 for the latent path); only the last section depends on it
+__host__ __device__ inline WsLayout ws_layout(int batch, int rows, int capacity, int dv = kDv)
 {
     WsLayout w;
     size_t off = 0;
@@ -67,7 +70,7 @@ __host__ __device__ inline WsLayout ws_layout(int batch, int rows, int capacity)
     w.batch_split = off; off = align256(off + size_t(batch + 1) * sizeof(int32_t));
     w.items = off;       off = align256(off + size_t(capacity) * 4 * sizeof(int32_t));
     w.lse_part = off;    off = align256(off + size_t(capacity) * rows * sizeof(float));
-    w.o_part = off;      off = align256(off + size_t(capacity) * rows * kDv * sizeof(float));
+    w.o_part = off;      off = align256(off + size_t(capacity) * rows * dv * sizeof(float));
     w.total = off;
     return w;
 }
@@ -1165,9 +1168,13 @@ constexpr int kCombineChunk = 512;     // split weights staged in LDS per pass
 
 constexpr int kCombineFast = 24;       // rows with at most this many splits: one memory round trip
 
-__global__ void __launch_bounds__(kCombineThreads) combine_kernel(FwdArgs a)
+template <int DV>
+__global__ void __launch_bounds__(kCombineThreads) combine_kernel_t(FwdArgs a)
 {
-    const WsLayout lay = ws_layout(a.batch, a.rows, a.capacity);
+    constexpr int VW = DV / kCombineThreads;   // dims per thread: 4 (latent path) or 1
+    static_assert(VW == 4 || VW == 1, "512 or 128 value dims");
+    using VT = typename std::conditional<VW == 4, f32x4, float>::type;
+    const WsLayout lay = ws_layout(a.batch, a.rows, a.capacity, DV);
     const int32_t* header = reinterpret_cast<const int32_t*>(a.ws + lay.header);
     const int gr = blockIdx.x;                 // global row = b * rows + r
     const int t = threadIdx.x;
@@ -1189,8 +1196,8 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(FwdArgs a)
     const int n = s1 - s0;
     const float* lse_part = reinterpret_cast<const float*>(a.ws + lay.lse_part);
     const float* o_part = reinterpret_cast<const float*>(a.ws + lay.o_part);
-    const float* op = o_part + ((size_t)s0 * a.rows + r) * kDv + 4 * t;   // split s0, this thread's dims
-    const size_t stride = (size_t)a.rows * kDv;                           // between splits
+    const float* op = o_part + ((size_t)s0 * a.rows + r) * DV + VW * t;   // split s0, this thread's dims
+    const size_t stride = (size_t)a.rows * DV;                           // between splits
 
     __shared__ float w[kCombineChunk];
     __shared__ float red_m[kCombineThreads / 64];
@@ -1198,11 +1205,11 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(FwdArgs a)
 
     // few splits: issue every partial-row load together with the LSE loads, before any wait
     const bool fast = n <= kCombineFast;
-    f32x4 ov[kCombineFast];
+    VT ov[kCombineFast];
     if (fast) {
 #pragma unroll
         for (int i = 0; i < kCombineFast; ++i)
-            if (i < n) ov[i] = *reinterpret_cast<const f32x4*>(op + i * stride);
+            if (i < n) ov[i] = *reinterpret_cast<const VT*>(op + i * stride);
     }
 
     // M = max_s LSE_s (NaN anywhere poisons the row)
@@ -1232,7 +1239,7 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(FwdArgs a)
     poison |= (nan != 0);
 
     // weights exp(LSE_s - M) through LDS, then the weighted sum of the partial rows
-    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    VT o{};
     float W = 0.f;
     if (fast) {
         if (t < n) w[t] = (poison || M == -__builtin_inff()) ? 0.f : expf(my_lse - M);
@@ -1254,36 +1261,39 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(FwdArgs a)
             const float* oc = op + (size_t)(c0 - s0) * stride;
             int i = 0;
             for (; i + 4 <= nc; i += 4) {
-                const f32x4 v0 = *reinterpret_cast<const f32x4*>(oc + (i + 0) * stride);
-                const f32x4 v1 = *reinterpret_cast<const f32x4*>(oc + (i + 1) * stride);
-                const f32x4 v2 = *reinterpret_cast<const f32x4*>(oc + (i + 2) * stride);
-                const f32x4 v3 = *reinterpret_cast<const f32x4*>(oc + (i + 3) * stride);
+                const VT v0 = *reinterpret_cast<const VT*>(oc + (i + 0) * stride);
+                const VT v1 = *reinterpret_cast<const VT*>(oc + (i + 1) * stride);
+                const VT v2 = *reinterpret_cast<const VT*>(oc + (i + 2) * stride);
+                const VT v3 = *reinterpret_cast<const VT*>(oc + (i + 3) * stride);
                 o += w[i] * v0 + w[i + 1] * v1 + w[i + 2] * v2 + w[i + 3] * v3;
                 W += (w[i] + w[i + 1]) + (w[i + 2] + w[i + 3]);
             }
             for (; i < nc; ++i) {
-                o += w[i] * *reinterpret_cast<const f32x4*>(oc + i * stride);
+                o += w[i] * *reinterpret_cast<const VT*>(oc + i * stride);
                 W += w[i];
             }
         }
     }
     float lse_out;
     if (poison) {
-        const float qnan = __builtin_nanf("");
-        o = f32x4{qnan, qnan, qnan, qnan};
-        lse_out = qnan;
+        o = VT{} + __builtin_nanf("");
+        lse_out = __builtin_nanf("");
     } else if (M == -__builtin_inff()) {
         lse_out = -__builtin_inff();
     } else {
         o *= 1.f / W;
         lse_out = M + logf(W);
     }
-    ushort4 ob;
-    ob.x = f32_to_bf16_rne(o[0]);
-    ob.y = f32_to_bf16_rne(o[1]);
-    ob.z = f32_to_bf16_rne(o[2]);
-    ob.w = f32_to_bf16_rne(o[3]);
-    *reinterpret_cast<ushort4*>(a.out + (size_t)gr * kDv + 4 * t) = ob;
+    if constexpr (VW == 4) {
+        ushort4 ob;
+        ob.x = f32_to_bf16_rne(o[0]);
+        ob.y = f32_to_bf16_rne(o[1]);
+        ob.z = f32_to_bf16_rne(o[2]);
+        ob.w = f32_to_bf16_rne(o[3]);
+        *reinterpret_cast<ushort4*>(a.out + (size_t)gr * DV + 4 * t) = ob;
+    } else {
+        a.out[(size_t)gr * DV + t] = f32_to_bf16_rne(o);
+    }
     if (t == 0) a.lse[gr] = lse_out;
 }
 

@@ -87,14 +87,17 @@ def make_case(name: str, batch: int, s_q: int, heads: int, seqlen, seed: int, *,
               causal: bool = False, pool_pages: int | None = None, identity_table: bool = False,
               outlier_frac: float = 0.0, outlier_scale: float = 8.0,
               softmax_scale: float = 1.0 / np.sqrt(192.0), poison: bool = True,
-              table_slack: int = 0, zero_q: bool = False) -> DecodeCase:
+              table_slack: int = 0, zero_q: bool = False, row_dims: int = D_K,
+              q_dims: int | None = None) -> DecodeCase:
     """Build one seeded case (recipe in the module docstring).
 
     ``seqlen`` is an int (every sequence), a (lo, hi) inclusive range, or a list
     of per-sequence lengths.  ``table_slack`` adds unused -1 columns to the
     block table; ``zero_q`` replaces Q by zeros after drawing it (the stream
-    stays the same).
+    stays the same).  ``row_dims`` / ``q_dims`` set the cache-row and query
+    widths (576 / 576 for the latent path; the GQA path uses 320 / 192).
     """
+    q_dims = row_dims if q_dims is None else q_dims
     rng = np.random.default_rng(seed)
     if isinstance(seqlen, (tuple,)) and len(seqlen) == 2:
         lens = rng.integers(int(seqlen[0]), int(seqlen[1]), endpoint=True, size=batch).astype(np.int64)
@@ -109,16 +112,16 @@ def make_case(name: str, batch: int, s_q: int, heads: int, seqlen, seed: int, *,
     pool = need if pool_pages is None else int(pool_pages)
     assert pool >= max(need, 1), "pool too small for the requested lengths"
 
-    qf = rng.standard_normal((batch, s_q, heads, D_K), dtype=np.float32)
+    qf = rng.standard_normal((batch, s_q, heads, q_dims), dtype=np.float32)
     q_bits = f32_to_bf16_bits(qf)
     del qf
     if zero_q:
         q_bits[...] = 0
 
-    cache = np.empty((pool, PAGE_SIZE, D_K), dtype=np.uint16)
+    cache = np.empty((pool, PAGE_SIZE, row_dims), dtype=np.uint16)
     for c0 in range(0, pool, _CHUNK_PAGES):
         c1 = min(pool, c0 + _CHUNK_PAGES)
-        cache[c0:c1] = f32_to_bf16_bits(rng.standard_normal((c1 - c0, PAGE_SIZE, D_K), dtype=np.float32))
+        cache[c0:c1] = f32_to_bf16_bits(rng.standard_normal((c1 - c0, PAGE_SIZE, row_dims), dtype=np.float32))
 
     perm = np.arange(pool, dtype=np.int64) if identity_table else rng.permutation(pool)
     max_pages = int(pages.max()) if batch else 0

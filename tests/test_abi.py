@@ -155,6 +155,25 @@ def test_absorb_argument_errors(L):
     assert L.mla_unabsorb_o(f, f, 1, 2, 256, f, None) == -2
 
 
+def test_gqa_argument_errors(L):
+    f = P(FAKE)
+    n = ctypes.c_size_t(0)
+    args = lambda **kw: {**dict(q=FAKE, kv=FAKE, bt=FAKE, bs=4, sl=FAKE, b=1, s_q=2, h=16, np_=4, ps=64, sc=0.07, c=1,
+                                ws=FAKE, wsb=1 << 20, out=FAKE, lse=FAKE), **kw}
+    call = lambda a: L.mla_gqa_decode_fwd(P(a["q"]), P(a["kv"]), P(a["bt"]), a["bs"], P(a["sl"]), a["b"], a["s_q"],
+                                           a["h"], a["np_"], a["ps"], ctypes.c_float(a["sc"]), a["c"], P(a["ws"]),
+                                           a["wsb"], P(a["out"]), P(a["lse"]), None)
+    for kw, code in [(dict(q=0), -1), (dict(kv=0), -1), (dict(b=0), -1), (dict(c=3), -1), (dict(sc=float("inf")), -1),
+                     (dict(q=FAKE + 2), -1), (dict(h=32), -2), (dict(s_q=3), -2), (dict(ps=32), -2)]:
+        assert call(args(**kw)) == code, kw
+    assert L.mla_gqa_decode_workspace_size(1, 1, 16, None) == -1
+    assert L.mla_gqa_decode_workspace_size(1, 1, 128, ctypes.byref(n)) == -2
+    assert L.mla_gqa_decode_plan(None, 1, 1, 16, f, 1 << 20, None) == -1
+    assert L.mla_gqa_decode_plan(f, 1, 2, 64, f, 1 << 20, None) == -2
+    if not __import__("torch").cuda.is_available():
+        assert call(args()) == -4
+
+
 def test_valid_arguments_without_a_gpu_report_no_device(L):
     import torch
     if torch.cuda.is_available():
