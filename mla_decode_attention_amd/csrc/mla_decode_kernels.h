@@ -79,8 +79,11 @@ enum HeaderField { kHMagic = 0, kHBatch, kHSq, kHHeads, kHItems, kHCapacity, kHR
 
 // =============================================================================================
 // Plan: balanced split of every sequence's pages into at most `gx + batch` work items.
-// One workgroup; the chunk size is ceil(total pages / gx) so that about gx items (one per
-// resident workgroup slot of the split kernel) carry equal page counts.
+// One workgroup.  A sequence of p pages gets ceil(p / chunk) items of at most `chunk` pages; the
+// chunk is the smallest one whose item count fits the gx resident workgroup slots of the split
+// kernel (one wave of workgroups: with uneven lengths, ceil(total / gx) rounds up to a few items
+// more than gx, and those would run as a second wave).  With batch >= gx every sequence is one
+// item.
 // =============================================================================================
 constexpr int kPlanThreads = 1024;
 
@@ -111,13 +114,48 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(const int32_t* __res
         ws_len[b] = L;
         mine += pages_of(L);
     }
-    for (int o = 32; o > 0; o >>= 1) mine += __shfl_xor(mine, o);
-    if (lane == 0) red[wid] = mine;
+    // block-wide sum (every thread gets it); two barriers so that red[] can be reused
+    auto block_sum = [&](long long v) {
+        for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+        __syncthreads();
+        if (lane == 0) red[wid] = v;
+        __syncthreads();
+        long long t = 0;
+        for (int w = 0; w < kPlanThreads / 64; ++w) t += red[w];
+        return t;
+    };
     if (tid == 0) scan_carry = 0;
-    __syncthreads();
-    long long total = 0;
-    for (int w = 0; w < kPlanThreads / 64; ++w) total += red[w];
-    long long chunk = (total + gx - 1) / (gx > 0 ? gx : 1);
+    const long long total = block_sum(mine);
+    auto items_for = [&](long long c) {
+        long long n = 0;
+        for (int b = tid; b < batch; b += kPlanThreads) n += (pages_of(len_of(b)) + c - 1) / c;
+        return block_sum(n);
+    };
+    const long long slots = gx > 0 ? gx : 1;
+    long long chunk;
+    if (slots > batch) {
+        // items(c) <= total / c + batch, so c = ceil(total / (slots - batch)) always fits
+        long long lo = (total + slots - 1) / slots, hi = (total + (slots - batch) - 1) / (slots - batch);
+        if (lo < 1) lo = 1;
+        if (hi < lo) hi = lo;
+        while (lo < hi) {   // uniform across the workgroup: every thread takes the same branch
+            const long long mid = (lo + hi) / 2;
+            if (items_for(mid) <= slots)
+                hi = mid;
+            else
+                lo = mid + 1;
+        }
+        chunk = lo;
+    } else {
+        long long mx = 0;
+        for (int b = tid; b < batch; b += kPlanThreads) mx = max(mx, (long long)pages_of(len_of(b)));
+        for (int o = 32; o > 0; o >>= 1) mx = max(mx, __shfl_xor(mx, o));
+        __syncthreads();
+        if (lane == 0) red[wid] = mx;
+        __syncthreads();
+        for (int w = 0; w < kPlanThreads / 64; ++w) mx = max(mx, red[w]);
+        chunk = mx;
+    }
     if (chunk < 1) chunk = 1;
 
     // per-sequence split counts, exclusive prefix sum in blocks of kPlanThreads

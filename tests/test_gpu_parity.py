@@ -138,7 +138,8 @@ def test_workspace_too_small_is_reported(dev):
 
 
 def test_plan_covers_every_page_once(dev):
-    """Read the plan back: items tile each sequence's pages exactly once, in balanced chunks."""
+    """Read the plan back: items tile each sequence's pages exactly once, in balanced chunks of the
+    smallest size that fits one wave of split workgroups."""
     import torch
 
     import mla_decode_attention_amd as mla
@@ -175,7 +176,10 @@ def test_plan_covers_every_page_once(dev):
             covered = [p for it in its for p in range(it[1], it[2])]
             assert covered == list(range(pages)), (b, L)
             sizes += (its[:, 2] - its[:, 1]).tolist()
-        total = sum((L + 63) // 64 for L in lens)
-        chunk = -(-total // (cap - len(lens)))
-        assert max(sizes) <= max(chunk, 1)
+        # the chunk is the smallest page count whose per-sequence split counts fit the
+        # cap - batch workgroup slots (one wave of split workgroups)
+        slots = cap - len(lens)
+        pages = [(L + 63) // 64 for L in lens]
+        chunk = next(c for c in range(1, max(pages) + 2) if sum(-(-p // c) for p in pages) <= slots)
+        assert n_items <= slots and max(sizes) <= chunk
         log(f"plan s_q={s_q} h={heads}: {n_items} items (capacity {cap}), chunk {chunk}, sizes {min(sizes)}..{max(sizes)}")
