@@ -213,7 +213,7 @@ def main() -> int:
     ap.add_argument("--cpu-sample-seqs", type=int, default=16)
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (default: min(16, usable cores))")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum timed oracle work")
-    ap.add_argument("--no-extras", action="store_true", help="skip the append and sparse-decode timings")
+    ap.add_argument("--no-extras", action="store_true", help="skip the timings of the other entry points (extras)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this size (for scaling PMC byte counters)")
     args = ap.parse_args()
@@ -304,7 +304,7 @@ def main() -> int:
     split_gbs = kv_q_bytes / (split_avg_ms * 1e-3) / 1e9
     mfma_util = step_flops / (ms_per_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS
     split_flops = step_flops   # every FLOP of the step is in the split kernel
-    split_name = "split_wide_kernel" if s_q * h >= 128 else "split_kernel"
+    split_name = "split_wide_kernel" if s_q * h >= 32 else "split_kernel"
 
     if args.calib_copy_mib > 0:
         n = args.calib_copy_mib * (1 << 20) // 4
@@ -321,7 +321,7 @@ def main() -> int:
 
     extras = None
     if not args.no_extras:
-        log("extras: cache append + RoPE, top-2048 sparse decode")
+        log("extras: sparse top-k, absorption, GQA path, cache append")
         extras = measure_extras(mla, case, dev, q, cache, bt, sl, K)
         log(f"extras: {extras}")
 
