@@ -214,6 +214,9 @@ def main() -> int:
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (default: min(16, usable cores))")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum timed oracle work")
     ap.add_argument("--no-extras", action="store_true", help="skip the timings of the other entry points (extras)")
+    ap.add_argument("--flush-mib", type=int, default=0,
+                    help="also time each step alone after overwriting this many MiB of scratch memory, so the "
+                         "cache is read from HBM and not from the last-level cache (256 MB on MI355X)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this size (for scaling PMC byte counters)")
     args = ap.parse_args()
@@ -297,6 +300,27 @@ def main() -> int:
     log(f"step {ms_per_step * 1e3:.1f} us (split kernel {split_avg_ms * 1e3:.1f} us avg, "
         f"median {np.median(split_ms) * 1e3:.1f} us), plan {plan_us:.1f} us")
 
+    flushed = None
+    if args.flush_mib > 0:
+        # each step alone, after a fill kernel has overwritten flush_mib MiB (outside the timed region)
+        scratch = torch.empty(args.flush_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+        e = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+        torch.cuda.synchronize()
+        for k in range(K):
+            scratch.fill_(float(k))
+            e[k][0].record(stream)
+            mla.fwd_split(q, cache, bt, sl, case.softmax_scale, case.causal, ws)
+            e[k][1].record(stream)
+            mla.fwd_combine(sl, bt.shape[1], s_q, h, ws, out, lse)
+            e[k][2].record(stream)
+        torch.cuda.synchronize()
+        f_step = float(np.median([e[k][0].elapsed_time(e[k][2]) for k in range(K)]))
+        f_split = float(np.median([e[k][0].elapsed_time(e[k][1]) for k in range(K)]))
+        del scratch
+        flushed = {"flush_mib": args.flush_mib, "steps": K, "median_us_per_step": round(f_step * 1e3, 2),
+                   "median_split_us": round(f_split * 1e3, 2)}
+        log(f"flushed: step median {f_step * 1e3:.1f} us, split median {f_split * 1e3:.1f} us")
+
     step_bytes = W.algorithmic_bytes(case.seqlens, b, s_q, h)
     step_flops = W.algorithmic_flops(case.seqlens, s_q, h, case.causal)
     kv_q_bytes = int(case.seqlens.astype(np.int64).sum()) * W.ROW_BYTES + b * s_q * h * 576 * 2
@@ -305,6 +329,9 @@ def main() -> int:
     mfma_util = step_flops / (ms_per_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS
     split_flops = step_flops   # every FLOP of the step is in the split kernel
     split_name = "split_wide_kernel" if s_q * h >= 32 else "split_kernel"
+    if flushed is not None:
+        flushed["TB/s"] = round(step_bytes / (flushed["median_us_per_step"] * 1e-6) / 1e12, 4)
+        flushed["split_GB/s"] = round(kv_q_bytes / (flushed["median_split_us"] * 1e-6) / 1e9, 1)
 
     if args.calib_copy_mib > 0:
         n = args.calib_copy_mib * (1 << 20) // 4
@@ -365,6 +392,8 @@ def main() -> int:
         "parity_vs_oracle": parity,
         "extras": extras,
     }
+    if flushed is not None:
+        line["flushed"] = flushed
     print(json.dumps(line), flush=True)
     return 0
 
