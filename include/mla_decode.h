@@ -70,8 +70,11 @@ int mla_decode_workspace_size(int batch, int s_q, int num_heads, size_t *bytes);
  * Split-KV plan: reads seqlens on the device and writes into `workspace` a
  * balanced partition of all sequences' cache pages into work items sized for
  * the device's compute units (a long sequence is cut into several items whose
- * partial results mla_decode_fwd merges by LSE).  One plan serves every layer
- * of a decode step as long as seqlens, batch, s_q and num_heads are unchanged.
+ * partial results mla_decode_fwd merges by LSE).  Each item lies within one
+ * sequence and holds at most `chunk` pages, where chunk is the smallest size
+ * whose item count fits the resident workgroups of one launch.  One plan serves
+ * every layer of a decode step as long as seqlens, batch, s_q and num_heads are
+ * unchanged.
  *   seqlens    int32 [batch], device: context length L_b >= 0 of each sequence,
  *              counting the s_q new tokens
  *   workspace  device buffer of at least mla_decode_workspace_size() bytes; its
