@@ -137,13 +137,23 @@ def test_workspace_too_small_is_reported(dev):
     assert e.value.status == -3
 
 
-def test_plan_covers_every_page_once(dev):
+def _long_batch_lens(batch, seed):
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(0, 300, batch)
+    lens[::7] = 0
+    lens[3::11] = rng.integers(1000, 3000, len(lens[3::11]))
+    return [int(x) for x in lens]
+
+
+@pytest.mark.parametrize("lens_kind", ["mixed", "batch_beyond_slots"])
+def test_plan_covers_every_page_once(dev, lens_kind):
     """Read the plan back: items tile each sequence's pages exactly once, in balanced chunks of the
-    smallest size that fits one wave of split workgroups."""
+    smallest size that fits one wave of split workgroups (one item per sequence once the batch
+    reaches the number of workgroup slots)."""
     import torch
 
     import mla_decode_attention_amd as mla
-    lens = [0, 1, 64, 65, 5000, 65536, 12345, 3]
+    lens = [0, 1, 64, 65, 5000, 65536, 12345, 3] if lens_kind == "mixed" else _long_batch_lens(300, 41)
     sl = torch.tensor(lens, dtype=torch.int32, device=dev)
     for s_q, heads in [(1, 16), (2, 16), (1, 128), (2, 128)]:
         ws = torch.zeros(mla.workspace_size(len(lens), s_q, heads), dtype=torch.uint8, device=dev)
@@ -180,6 +190,20 @@ def test_plan_covers_every_page_once(dev):
         # cap - batch workgroup slots (one wave of split workgroups)
         slots = cap - len(lens)
         pages = [(L + 63) // 64 for L in lens]
-        chunk = next(c for c in range(1, max(pages) + 2) if sum(-(-p // c) for p in pages) <= slots)
-        assert n_items <= slots and max(sizes) <= chunk
+        if slots > len(lens):
+            chunk = next(c for c in range(1, max(pages) + 2) if sum(-(-p // c) for p in pages) <= slots)
+            assert n_items <= slots and max(sizes) <= chunk
+        else:   # every sequence is one item
+            chunk = max(pages)
+            assert n_items == sum(p > 0 for p in pages)
         log(f"plan s_q={s_q} h={heads}: {n_items} items (capacity {cap}), chunk {chunk}, sizes {min(sizes)}..{max(sizes)}")
+
+
+@pytest.mark.parametrize("heads,s_q,batch", [(16, 1, 300), (16, 2, 300), (128, 1, 140)])
+def test_batch_beyond_workgroup_slots(dev, heads, s_q, batch):
+    """More sequences than resident split workgroups: the plan makes one item per sequence and the
+    extra workgroups run as later waves; every row still matches the oracle."""
+    lens = _long_batch_lens(batch, 42 + heads + s_q)
+    case = make_case(f"batch{batch}_h{heads}_sq{s_q}", batch=batch, s_q=s_q, heads=heads, seqlen=lens, seed=43,
+                     causal=s_q == 2)
+    full_parity(case, dev)
