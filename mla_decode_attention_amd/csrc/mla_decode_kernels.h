@@ -1205,6 +1205,7 @@ constexpr int kCombineThreads = 128;   // one (sequence, row) per workgroup, 4 d
 constexpr int kCombineChunk = 512;     // split weights staged in LDS per pass
 
 constexpr int kCombineFast = 24;       // rows with at most this many splits: one memory round trip
+constexpr int kCombineFastNarrow = 64; // the same for 128-wide rows (one register per split)
 
 template <int DV>
 __global__ void __launch_bounds__(kCombineThreads) combine_kernel_t(FwdArgs a)
@@ -1242,11 +1243,13 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel_t(FwdArgs a)
     __shared__ int red_nan[kCombineThreads / 64];
 
     // few splits: issue every partial-row load together with the LSE loads, before any wait
-    const bool fast = n <= kCombineFast;
-    VT ov[kCombineFast];
+    constexpr int FAST = VW == 4 ? kCombineFast : kCombineFastNarrow;
+    static_assert(FAST <= kCombineThreads, "one LSE per thread on the fast path");
+    const bool fast = n <= FAST;
+    VT ov[FAST];
     if (fast) {
 #pragma unroll
-        for (int i = 0; i < kCombineFast; ++i)
+        for (int i = 0; i < FAST; ++i)
             if (i < n) ov[i] = *reinterpret_cast<const VT*>(op + i * stride);
     }
 
@@ -1284,7 +1287,7 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel_t(FwdArgs a)
         __syncthreads();
         if (!poison && M != -__builtin_inff()) {
 #pragma unroll
-            for (int i = 0; i < kCombineFast; ++i)
+            for (int i = 0; i < FAST; ++i)
                 if (i < n) {
                     o += w[i] * ov[i];
                     W += w[i];
