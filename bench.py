@@ -9,7 +9,9 @@ layers of a model, so it is timed separately and reported as ``plan_us``.
 
 Default workload: batch 16, s_q 1, 16 heads, 65536-token contexts over a
 shuffled pool of 64-token bf16 pages (about 1.2 GB of cache), values N(0,1).
-Prints ONE JSON line on stdout; progress goes to stderr.
+Prints ONE JSON line on stdout; progress goes to stderr.  ``extras`` holds the
+timings of the library's other entry points; ``--flush-mib`` adds per-step
+timings taken after a last-level-cache flush.
 """
 from __future__ import annotations
 
@@ -83,9 +85,10 @@ def cpu_baseline(case, o_gpu, lse_gpu, n_seqs: int, threads: int, min_seconds: f
 
 
 def measure_extras(mla, case, dev, q, cache, bt, sl, steps: int):
-    """Time the steps either side of the decode path on the same inputs: the cache append with
-    rotary embedding of the s_q new tokens, and a top-2048 sparse decode over the same cache (with
-    a parity check of sampled query tokens against the fp64 oracle)."""
+    """Time the library's other entry points: a top-2048 sparse decode over the same cache (with a
+    parity check of sampled query tokens against the fp64 oracle), the absorption and
+    un-absorption products, the GQA path on the MTP shape beside the latent path on the same
+    lengths (with sampled parity), and the cache append with rotary embedding of the new tokens."""
     import numpy as np
     import torch
 
