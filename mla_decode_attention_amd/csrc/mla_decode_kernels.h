@@ -272,6 +272,28 @@ struct FwdArgs {
     int sparse_sq;
 };
 
+// The plan header and one work item's record, read together in one memory round trip: the
+// record index is clamped into the item array, so the read stays in bounds whatever the header
+// holds, and the checks use no short-circuit (which would put each header field behind its own
+// load-and-wait).  ok: the header matches this launch and the item exists.
+struct PlanItem {
+    bool ok;
+    i32x4 it;   // (sequence, first page, end page, split index)
+};
+
+__device__ inline PlanItem read_plan_item(const FwdArgs& a, const WsLayout& lay, int item)
+{
+    PlanItem p;
+    p.it = reinterpret_cast<const i32x4*>(a.ws + lay.items)[min(item, a.capacity - 1)];
+    const i32x4 h0 = *reinterpret_cast<const i32x4*>(a.ws + lay.header);
+    const int2 h1 = *reinterpret_cast<const int2*>(a.ws + lay.header + 4 * sizeof(int32_t));   // items, capacity
+    // the record's sequence index takes part in the check, so its load is issued with the header's
+    p.ok = (h0[kHMagic] == kPlanMagic) & (h0[kHBatch] == a.batch) & (h0[kHSq] == a.s_q) &
+           (h0[kHHeads] == a.heads) & (h1.y == a.capacity) & (item < h1.x) &
+           ((unsigned)p.it[0] < (unsigned)a.batch);
+    return p;
+}
+
 __device__ inline const MLA_LDS i16x4* lds_i16x4(const void* p)
 {
     return (const MLA_LDS i16x4*)(const MLA_LDS char*)p;
@@ -321,6 +343,13 @@ struct PageWindow {
         base = -1;
         val = 0;
     }
+    // fill the window at idx without waiting: the first page() call waits for this load alone
+    __device__ inline void prefetch(int idx, int lane)
+    {
+        base = idx;
+        const int v = row[min(idx + lane, len - 1)];   // no branch: every lane loads in bounds
+        val = (idx + lane < len) ? v : -1;
+    }
     __device__ inline int page(int idx, int lane)
     {
         if (base < 0 || idx < base || idx >= base + 64) {
@@ -365,17 +394,21 @@ __global__ void __launch_bounds__(C::THREADS) split_kernel(FwdArgs a)
     const int lg = lane >> 4;               // lane group (MFMA k / row quad)
 
     const WsLayout lay = ws_layout(a.batch, a.rows, a.capacity);
-    const int32_t* header = reinterpret_cast<const int32_t*>(a.ws + lay.header);
-    if (header[kHMagic] != kPlanMagic || header[kHBatch] != a.batch || header[kHSq] != a.s_q ||
-        header[kHHeads] != a.heads || header[kHCapacity] != a.capacity)
-        return;  // the combine kernel reports the mismatch
+    // the arguments of the prologue's address computations come in with the first ones
+    asm volatile("" ::"s"(a.q), "s"(a.block_table), "s"(a.seqlens), "s"(a.bt_stride));
     const int item = blockIdx.x;
-    if (item >= header[kHItems]) return;
-    const i32x4 it = reinterpret_cast<const i32x4*>(a.ws + lay.items)[item];
+    const PlanItem pi = read_plan_item(a, lay, item);
+    if (!pi.ok) return;   // a plan mismatch is reported by the combine kernel
+    const i32x4 it = pi.it;
     const int b = it[0];              // sequence (sparse: query token b_real * sparse_sq + i)
-    const int32_t plan_L = reinterpret_cast<const int32_t*>(a.ws + lay.seqlens)[b];
     // dense: L = context length; sparse: L = index slots, Lc = the context the indices point into
     const int b_tab = SPARSE ? b / a.sparse_sq : b;
+    // The first block-table window, the lengths and Q go out together (one round trip) before
+    // anything waits for them; every address here is valid once the plan matched.
+    PageWindow pw;
+    pw.init(a.block_table + (size_t)b_tab * a.bt_stride, a.bt_stride);
+    if constexpr (!SPARSE) pw.prefetch(it[1], lane);
+    const int32_t plan_L = reinterpret_cast<const int32_t*>(a.ws + lay.seqlens)[b];
     const int Lc = a.seqlens[b_tab];
     const int L = SPARSE ? a.topk : Lc;
     float* lse_part = reinterpret_cast<float*>(a.ws + lay.lse_part) + (size_t)item * a.rows;
@@ -384,16 +417,6 @@ __global__ void __launch_bounds__(C::THREADS) split_kernel(FwdArgs a)
     const int rb = blockIdx.y * C::RB + rbl;          // global 16-row block
     const int row0 = rb * 16;
     const int qi = row0 / a.heads;                    // query token of this block (heads % 16 == 0)
-    const bool bad_seq = (L != plan_L) || L < 0 || Lc < 0 || (long long)Lc > (long long)kPage * a.bt_stride;
-    if (bad_seq) {
-        if (tid < C::RB * 16) lse_part[blockIdx.y * C::RB * 16 + tid] = __builtin_nanf("");
-        return;
-    }
-    const int n_vis = (!SPARSE && a.causal) ? min(max(L - a.s_q + 1 + qi, 0), L) : L;
-    const int tok_begin = it[1] * kPage;
-    const int tok_end = min(it[2] * kPage, L);
-    const int n_tiles = (tok_end - tok_begin + C::TT - 1) / C::TT;
-    const int n_it = (n_tiles + C::NG - 1) / C::NG;
 
     // ---- Q^T operand (B of the score MFMA): lane (row lr, group lg) holds q[row][32j+8lg .. +8]
     bf16x8 qop[kKSteps];
@@ -403,11 +426,16 @@ __global__ void __launch_bounds__(C::THREADS) split_kernel(FwdArgs a)
 #pragma unroll
         for (int j = 0; j < kKSteps; ++j)
             qop[j] = *reinterpret_cast<const bf16x8*>(qrow + 32 * j + 8 * lg);
-        // Consume Q here so the compiler's vmcnt waits for these loads land before the tile
-        // loop, not inside it (where they would also wait for the tile loads in flight).
-#pragma unroll
-        for (int j = 0; j < kKSteps; ++j) asm volatile("" ::"v"(qop[j]));
     }
+
+    // A sequence whose length disagrees with the plan or the table gets no tiles and a NaN LSE
+    // (no early exit: a branch here would make the loads above wait one after another).
+    const bool bad_seq = (L != plan_L) | (L < 0) | (Lc < 0) | ((long long)Lc > (long long)kPage * a.bt_stride);
+    const int n_vis = (!SPARSE && a.causal) ? min(max(L - a.s_q + 1 + qi, 0), L) : L;
+    const int tok_begin = it[1] * kPage;
+    const int tok_end = min(it[2] * kPage, L);
+    const int n_tiles = bad_seq ? 0 : (tok_end - tok_begin + C::TT - 1) / C::TT;
+    const int n_it = (n_tiles + C::NG - 1) / C::NG;
 
     // ---- this wave's load units of a tile: unit u covers tile bytes [1024 u, 1024 u + 1024);
     // lane l takes 16-B chunk P = 64 u + l of row r = P / 72, which goes to LDS byte 16 P + 32 r.
@@ -423,9 +451,7 @@ __global__ void __launch_bounds__(C::THREADS) split_kernel(FwdArgs a)
     }
     const int unit0 = wg * C::NPW;                           // first unit of this wave
     char* const group_stages = smem + gi * C::NS * C::LDS_TILE;
-    PageWindow pw;
-    pw.init(a.block_table + (size_t)b_tab * a.bt_stride, a.bt_stride);
-    bool bad_page = false;
+    bool bad_page = bad_seq;
 
     i32x4 rbuf[C::NR][C::NPW];
     // sparse: validity masks (bit r = index slot r of the tile names a row) of the tiles loaded but
@@ -688,6 +714,10 @@ __global__ void __launch_bounds__(C::THREADS) split_kernel(FwdArgs a)
     if constexpr (C::NR == 2) load_tile(1, Idx<1>{});
     store_tile(0, Idx<0>{});
     load_tile(C::NR, Idx<0>{});
+    // Consume Q here, so that no wait for it lands inside the tile loop (where it would also wait
+    // for the tile loads in flight)
+#pragma unroll
+    for (int j = 0; j < kKSteps; ++j) asm volatile("" ::"v"(qop[j]));
     if constexpr (C::GW > 1) __syncthreads();
     if constexpr (C::NR == 2) {
         for (int itn = 0; itn < n_it; itn += 2) {
@@ -821,13 +851,16 @@ __global__ void __launch_bounds__(C::THREADS) split_wide_kernel(FwdArgs a)
     const int rg = (x / 8) % G;
 
     const WsLayout lay = ws_layout(a.batch, a.rows, a.capacity);
-    const int32_t* header = reinterpret_cast<const int32_t*>(a.ws + lay.header);
-    if (header[kHMagic] != kPlanMagic || header[kHBatch] != a.batch || header[kHSq] != a.s_q ||
-        header[kHHeads] != a.heads || header[kHCapacity] != a.capacity)
-        return;  // the combine kernel reports the mismatch
-    if (item >= header[kHItems]) return;
-    const i32x4 it = reinterpret_cast<const i32x4*>(a.ws + lay.items)[item];
+    // the arguments of the prologue's address computations come in with the first ones
+    asm volatile("" ::"s"(a.q), "s"(a.block_table), "s"(a.seqlens), "s"(a.bt_stride));
+    const PlanItem pi = read_plan_item(a, lay, item);
+    if (!pi.ok) return;   // a plan mismatch is reported by the combine kernel
+    const i32x4 it = pi.it;
     const int b = it[0];
+    // the first block-table window and the lengths go out together (one round trip)
+    PageWindow pw;
+    pw.init(a.block_table + (size_t)b * a.bt_stride, a.bt_stride);
+    pw.prefetch(it[1], lane);
     const int L = a.seqlens[b];
     const int32_t plan_L = reinterpret_cast<const int32_t*>(a.ws + lay.seqlens)[b];
     float* lse_part = reinterpret_cast<float*>(a.ws + lay.lse_part) + (size_t)item * a.rows;
@@ -836,15 +869,13 @@ __global__ void __launch_bounds__(C::THREADS) split_wide_kernel(FwdArgs a)
     const int row_base = rg * C::RW;                  // first row of this group
     const int srow = row_base + 16 * w4 + lr;         // score waves: this lane's row
     const int qi = (row_base + 16 * w4) / a.heads;    // score waves: query token of the row block
-    const bool bad_seq = (L != plan_L) || L < 0 || (long long)L > (long long)kPage * a.bt_stride;
-    if (bad_seq) {
-        if (tid < C::RW) lse_part[row_base + tid] = __builtin_nanf("");
-        return;
-    }
+    // A sequence whose length disagrees with the plan or the table gets no tiles and a NaN LSE
+    // (no early exit: a branch here would make the loads above wait one after another).
+    const bool bad_seq = (L != plan_L) | (L < 0) | ((long long)L > (long long)kPage * a.bt_stride);
     const int n_vis = a.causal ? min(max(L - a.s_q + 1 + qi, 0), L) : L;
     const int tok_begin = it[1] * kPage;
     const int tok_end = min(it[2] * kPage, L);
-    const int n_tiles = (tok_end - tok_begin + C::TT - 1) / C::TT;
+    const int n_tiles = bad_seq ? 0 : (tok_end - tok_begin + C::TT - 1) / C::TT;
 
     // ---- tile staging, shared by both roles: the waves w and w + 4 move 8-row group w of every
     // tile, the score wave units 0 .. US-1 and the value wave units US .. 8 of the group.  Lane l
@@ -856,9 +887,7 @@ __global__ void __launch_bounds__(C::THREADS) split_wide_kernel(FwdArgs a)
         const int bnd = kChunksPerRow * (r0 + 1) - 64 * v;
         return v * 1024 + (kLdsRow - kRowBytes) * (r0 + (lane >= bnd ? 1 : 0)) + (int)lane16;
     };
-    PageWindow pw;
-    pw.init(a.block_table + (size_t)b * a.bt_stride, a.bt_stride);
-    bool bad_page = false;
+    bool bad_page = bad_seq;
     auto tile_rsrc = [&](int t) __attribute__((always_inline)) {
         const int t0 = tok_begin + t * C::TT;
         const int page = pw.page(t0 / kPage, lane);
@@ -1214,24 +1243,27 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel_t(FwdArgs a)
     static_assert(VW == 4 || VW == 1, "512 or 128 value dims");
     using VT = typename std::conditional<VW == 4, f32x4, float>::type;
     const WsLayout lay = ws_layout(a.batch, a.rows, a.capacity, DV);
+    // the arguments used below come in with the first ones
+    asm volatile("" ::"s"(a.ws), "s"(a.seqlens), "s"(a.out), "s"(a.lse), "s"(a.bt_stride));
     const int32_t* header = reinterpret_cast<const int32_t*>(a.ws + lay.header);
     const int gr = blockIdx.x;                 // global row = b * rows + r
     const int t = threadIdx.x;
     const int b = gr / a.rows;
     const int r = gr % a.rows;
-    const bool shape_ok = header[kHMagic] == kPlanMagic && header[kHBatch] == a.batch &&
-                          header[kHSq] == a.s_q && header[kHHeads] == a.heads &&
-                          header[kHCapacity] == a.capacity;
-    bool poison = !shape_ok;
-    int s0 = 0, s1 = 0;
-    if (shape_ok) {
-        const int L = a.seqlens[b];
-        const int plan_L = reinterpret_cast<const int32_t*>(a.ws + lay.seqlens)[b];
-        poison = (L != plan_L) || L < 0 || (long long)L > (long long)kPage * a.bt_stride;
-        const int32_t* bs = reinterpret_cast<const int32_t*>(a.ws + lay.batch_split);
-        s0 = bs[b];
-        s1 = bs[b + 1];
-    }
+    // header, lengths and this sequence's split range in one round trip (all lie inside the
+    // workspace and seqlens whatever the header holds); the checks use no short-circuit
+    const i32x4 h0 = reinterpret_cast<const i32x4*>(header)[0];
+    const int h_cap = header[kHCapacity];
+    const int L = a.seqlens[b];
+    const int plan_L = reinterpret_cast<const int32_t*>(a.ws + lay.seqlens)[b];
+    const int32_t* bs = reinterpret_cast<const int32_t*>(a.ws + lay.batch_split);
+    const int bs0 = bs[b], bs1 = bs[b + 1];
+    const bool shape_ok = (h0[kHMagic] == kPlanMagic) & (h0[kHBatch] == a.batch) & (h0[kHSq] == a.s_q) &
+                          (h0[kHHeads] == a.heads) & (h_cap == a.capacity);
+    const bool len_bad = (L != plan_L) | (L < 0) | ((long long)L > (long long)kPage * a.bt_stride);
+    bool poison = !shape_ok | len_bad;
+    const int s0 = shape_ok ? bs0 : 0;   // selects, not a branch: the loads above stay together
+    const int s1 = shape_ok ? bs1 : 0;
     const int n = s1 - s0;
     const float* lse_part = reinterpret_cast<const float*>(a.ws + lay.lse_part);
     const float* o_part = reinterpret_cast<const float*>(a.ws + lay.o_part);

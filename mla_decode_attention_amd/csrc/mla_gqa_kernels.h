@@ -61,26 +61,27 @@ __global__ void __launch_bounds__(kGqaThreads) gqa_split_kernel(FwdArgs a)
     const int lg = lane >> 4;
 
     const WsLayout lay = ws_layout(a.batch, a.rows, a.capacity, kGqaDv);
-    const int32_t* header = reinterpret_cast<const int32_t*>(a.ws + lay.header);
-    if (header[kHMagic] != kPlanMagic || header[kHBatch] != a.batch || header[kHSq] != a.s_q ||
-        header[kHHeads] != a.heads || header[kHCapacity] != a.capacity)
-        return;  // the combine kernel reports the mismatch
+    // the arguments of the prologue's address computations come in with the first ones
+    asm volatile("" ::"s"(a.q), "s"(a.block_table), "s"(a.seqlens), "s"(a.bt_stride));
     const int item = blockIdx.x;
-    if (item >= header[kHItems]) return;
-    const i32x4 it = reinterpret_cast<const i32x4*>(a.ws + lay.items)[item];
+    const PlanItem pi = read_plan_item(a, lay, item);
+    if (!pi.ok) return;   // a plan mismatch is reported by the combine kernel
+    const i32x4 it = pi.it;
     const int b = it[0];
+    // the first block-table window, the lengths and Q go out together (one round trip)
+    PageWindow pw;
+    pw.init(a.block_table + (size_t)b * a.bt_stride, a.bt_stride);
+    pw.prefetch(it[1], lane);
     const int L = a.seqlens[b];
     const int32_t plan_L = reinterpret_cast<const int32_t*>(a.ws + lay.seqlens)[b];
     float* lse_part = reinterpret_cast<float*>(a.ws + lay.lse_part) + (size_t)item * a.rows;
     float* o_part = reinterpret_cast<float*>(a.ws + lay.o_part) + (size_t)item * a.rows * kGqaDv;
-    const bool bad_seq = (L != plan_L) || L < 0 || (long long)L > (long long)kPage * a.bt_stride;
-    if (bad_seq) {
-        if (tid < a.rows) lse_part[tid] = __builtin_nanf("");
-        return;
-    }
+    // A sequence whose length disagrees with the plan or the table gets no tiles and a NaN LSE
+    // (no early exit: a branch here would make the loads above wait one after another).
+    const bool bad_seq = (L != plan_L) | (L < 0) | ((long long)L > (long long)kPage * a.bt_stride);
     const int tok_begin = it[1] * kPage;
     const int tok_end = min(it[2] * kPage, L);
-    const int n_tiles = (tok_end - tok_begin + kGqaTT - 1) / kGqaTT;
+    const int n_tiles = bad_seq ? 0 : (tok_end - tok_begin + kGqaTT - 1) / kGqaTT;
     const int n_it = (n_tiles + kGqaWaves - 1) / kGqaWaves;
     int n_vis[NRB];
 #pragma unroll
@@ -95,18 +96,12 @@ __global__ void __launch_bounds__(kGqaThreads) gqa_split_kernel(FwdArgs a)
 #pragma unroll
         for (int j = 0; j < kGqaKSteps; ++j) qop[rb][j] = *reinterpret_cast<const bf16x8*>(qrow + 32 * j + 8 * lg);
     }
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-        for (int j = 0; j < kGqaKSteps; ++j) asm volatile("" ::"v"(qop[rb][j]));
 
     // tiles: wave w takes tiles w, w + 4, ...; lane l of unit u moves 16-B chunk 64 u + l of the
     // tile (row (64 u + l) / 40) into the wave's own stage
     const uint32_t lane16 = (uint32_t)lane * 16u;
     char* const stage = smem + wave * C::STAGE;
-    PageWindow pw;
-    pw.init(a.block_table + (size_t)b * a.bt_stride, a.bt_stride);
-    bool bad_page = false;
+    bool bad_page = bad_seq;
     i32x4 rbuf[kGqaUnits];
     auto load_tile = [&](int itn) __attribute__((always_inline)) {
         const int k = itn * kGqaWaves + wave;
@@ -213,6 +208,12 @@ __global__ void __launch_bounds__(kGqaThreads) gqa_split_kernel(FwdArgs a)
     load_tile(0);
     store_tile(0);
     load_tile(1);
+    // Consume Q here, so that no wait for it lands inside the tile loop (where it would also wait
+    // for the tile loads in flight)
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+        for (int j = 0; j < kGqaKSteps; ++j) asm volatile("" ::"v"(qop[rb][j]));
     for (int itn = 0; itn < n_it; ++itn) {
         const int k = itn * kGqaWaves + wave;
         if (k < n_tiles) compute_tile(k);
