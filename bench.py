@@ -373,7 +373,10 @@ def main() -> int:
     extras = None
     if not args.no_extras:
         log("extras: sparse top-k, absorption, GQA path, cache append")
-        extras = measure_extras(mla, case, dev, q, cache, bt, sl, K)
+        try:
+            extras = measure_extras(mla, case, dev, q, cache, bt, sl, K)
+        except Exception as exc:   # the headline line stands without them
+            extras = {"error": f"{type(exc).__name__}: {exc}"}
         log(f"extras: {extras}")
 
     cpu, parity = None, None
@@ -384,8 +387,12 @@ def main() -> int:
             usable = os.cpu_count() or 1
         threads = args.cpu_threads or min(16, usable)
         log(f"cpu baseline: fp64 oracle on {threads} threads, {args.cpu_sample_seqs} sequences")
-        cpu, parity = cpu_baseline(case, o_gpu, lse_gpu, args.cpu_sample_seqs, threads, args.cpu_seconds)
-        log(f"cpu baseline {cpu['seconds']:.1f} s -> {cpu['value']:.3e} TB/s; parity {parity}")
+        try:
+            cpu, parity = cpu_baseline(case, o_gpu, lse_gpu, args.cpu_sample_seqs, threads, args.cpu_seconds)
+            log(f"cpu baseline {cpu['seconds']:.1f} s -> {cpu['value']:.3e} TB/s; parity {parity}")
+        except Exception as exc:   # reported in the line instead of losing it
+            cpu = {"error": f"{type(exc).__name__}: {exc}", "kind": "oracle"}
+            log(f"cpu baseline failed: {cpu['error']}")
 
     line = {
         "metric": "MLA decode achieved HBM TB/s (% of peak) + us/step, b16 h16 64K ctx",
