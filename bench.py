@@ -81,7 +81,18 @@ def cpu_baseline(case, o_gpu, lse_gpu, n_seqs: int, threads: int, min_seconds: f
                 sample=f"{n_seqs} of {case.batch} sequences, all {case.s_q * case.heads} query rows each "
                        f"({rows.size} rows, {sample_bytes / 1e6:.1f} MB algorithmic), run {reps}x, "
                        f"fp64 C oracle (OpenMP)",
-                seconds=round(dt, 2)), parity
+                seconds=round(dt, 2), cpu_model=_cpu_model(), host_cpus=os.cpu_count()), parity
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def measure_extras(mla, case, dev, q, cache, bt, sl, steps: int):
@@ -324,6 +335,22 @@ def main() -> int:
     log(f"step {ms_per_step * 1e3:.1f} us (split kernel {split_avg_ms * 1e3:.1f} us avg, "
         f"median {np.median(split_ms) * 1e3:.1f} us), plan {plan_us:.1f} us")
 
+    # context: a plain device-to-device copy of 1 GiB (torch's copy kernel), the streaming rate a
+    # simple kernel gets on this GPU (read + write bytes per second)
+    src = torch.empty(256 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(10):
+        dst.copy_(src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * src.numel() * 4 * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst
+    log(f"device copy probe: {copy_gbs:.0f} GB/s (read + write)")
+
     flushed = None
     if args.flush_mib > 0:
         # each step alone, after a fill kernel has overwritten flush_mib MiB (outside the timed region)
@@ -418,7 +445,8 @@ def main() -> int:
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(split_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(name), "avg_launch_us": round(split_avg_ms * 1e3, 2),
                      "algorithmic_bytes_per_launch": kv_q_bytes,
-                     "mfma_frac": round(split_flops / (split_avg_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
+                     "mfma_frac": round(split_flops / (split_avg_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "copy_probe_GB/s": round(copy_gbs, 1), "frac_of_copy_probe": round(split_gbs / copy_gbs, 4)},
         "cpu_baseline": cpu,
         "parity_vs_oracle": parity,
         "extras": extras,
