@@ -53,6 +53,35 @@ def measured_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def c_calls(mla, fn):
+    """Run fn once through the binding and return the C-ABI calls it made (function, marshalled
+    arguments), for replay in timed loops: the binding's argument checks cost host time comparable
+    to the shorter kernels, and a replayed call costs only the ctypes call itself."""
+    calls = []
+    real_lib = mla.lib
+
+    class _Recorder:
+        def __getattr__(self, name):
+            f = getattr(real_lib(), name)
+
+            def call(*args):
+                calls.append((f, args))
+                return f(*args)
+            return call
+    mla.lib = lambda: _Recorder()
+    try:
+        fn()
+    finally:
+        mla.lib = real_lib
+
+    def replay():
+        for f, a in calls:
+            status = f(*a)
+            if status != 0:
+                raise RuntimeError(f"C call failed with status {status}")
+    return replay
+
+
 def cpu_baseline(case, o_gpu, lse_gpu, n_seqs: int, threads: int, min_seconds: float):
     """Time the fp64 oracle on the host cores over the first n_seqs sequences (all their query rows),
     repeating the sample until at least min_seconds of CPU work have been timed."""
@@ -108,34 +137,14 @@ def measure_extras(mla, case, dev, q, cache, bt, sl, steps: int):
     b, s_q, h = case.batch, case.s_q, case.heads
 
     def timed(fn):
-        # The binding's argument checks cost host time comparable to these short kernels, so fn runs
-        # once through the binding to record the C-ABI calls it makes (function and marshalled
-        # arguments), and the timed loop replays those C calls directly.
-        calls = []
-        real_lib = mla.lib
-
-        class _Recorder:
-            def __getattr__(self, name):
-                f = getattr(real_lib(), name)
-
-                def call(*args):
-                    calls.append((f, args))
-                    return f(*args)
-                return call
-        mla.lib = lambda: _Recorder()
-        try:
-            fn()
-        finally:
-            mla.lib = real_lib
+        replay = c_calls(mla, fn)
         for _ in range(3):
-            for f, a in calls:
-                f(*a)
+            replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(steps):
-            for f, a in calls:
-                f(*a)
+            replay()
         e1.record(stream)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3 / steps
@@ -289,19 +298,23 @@ def main() -> int:
     log(f"inputs on device: cache {cache.numel() * 2 / 1e9:.3f} GB, workspace {ws.numel() / 1e6:.1f} MB")
 
     # plan (once per decode step for every layer): timed on its own
+    # Every timed loop below replays the C-ABI calls the binding makes (see c_calls).
     torch.cuda.synchronize()
     p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    mla.plan(sl, s_q, h, ws)
+    plan_c = c_calls(mla, lambda: mla.plan(sl, s_q, h, ws))
     p0.record(stream)
     for _ in range(10):
-        mla.plan(sl, s_q, h, ws)
+        plan_c()
     p1.record(stream)
     torch.cuda.synchronize()
     plan_us = p0.elapsed_time(p1) * 1e3 / 10
 
+    split_c = c_calls(mla, lambda: mla.fwd_split(q, cache, bt, sl, case.softmax_scale, case.causal, ws))
+    combine_c = c_calls(mla, lambda: mla.fwd_combine(sl, bt.shape[1], s_q, h, ws, out, lse))
+
     def step():
-        mla.fwd_split(q, cache, bt, sl, case.softmax_scale, case.causal, ws)
-        mla.fwd_combine(sl, bt.shape[1], s_q, h, ws, out, lse)
+        split_c()
+        combine_c()
 
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -326,9 +339,9 @@ def main() -> int:
     torch.cuda.synchronize()
     for k in range(K):
         ev_a[k].record(stream)
-        mla.fwd_split(q, cache, bt, sl, case.softmax_scale, case.causal, ws)
+        split_c()
         ev_b[k].record(stream)
-        mla.fwd_combine(sl, bt.shape[1], s_q, h, ws, out, lse)
+        combine_c()
     torch.cuda.synchronize()
     split_ms = [ev_a[k].elapsed_time(ev_b[k]) for k in range(K)]
     split_avg_ms = float(np.mean(split_ms))
@@ -360,9 +373,9 @@ def main() -> int:
         for k in range(K):
             scratch.fill_(float(k))
             e[k][0].record(stream)
-            mla.fwd_split(q, cache, bt, sl, case.softmax_scale, case.causal, ws)
+            split_c()
             e[k][1].record(stream)
-            mla.fwd_combine(sl, bt.shape[1], s_q, h, ws, out, lse)
+            combine_c()
             e[k][2].record(stream)
         torch.cuda.synchronize()
         f_step = float(np.median([e[k][0].elapsed_time(e[k][2]) for k in range(K)]))
