@@ -145,7 +145,21 @@ def _long_batch_lens(batch, seed):
     return [int(x) for x in lens]
 
 
-@pytest.mark.parametrize("lens_kind", ["mixed", "batch_beyond_slots"])
+def _plan_lens(kind):
+    rng = np.random.default_rng(47)
+    return {
+        "mixed": lambda: [0, 1, 64, 65, 5000, 65536, 12345, 3],
+        "batch_beyond_slots": lambda: _long_batch_lens(300, 41),
+        "all_empty": lambda: [0] * 9,
+        "one_huge": lambda: [0, 1, 262144, 5],
+        "many_tiny": lambda: [int(x) for x in rng.integers(1, 65, 200)],
+        "uneven_like_mtp": lambda: [int(x) for x in rng.integers(8192, 16385, 16)],
+        "batch_near_slots": lambda: [int(x) for x in rng.integers(0, 5000, 120)],
+    }[kind]()
+
+
+@pytest.mark.parametrize("lens_kind", ["mixed", "batch_beyond_slots", "all_empty", "one_huge", "many_tiny",
+                                       "uneven_like_mtp", "batch_near_slots"])
 def test_plan_covers_every_page_once(dev, lens_kind):
     """Read the plan back: items tile each sequence's pages exactly once, in balanced chunks of the
     smallest size that fits one wave of split workgroups (one item per sequence once the batch
@@ -153,7 +167,7 @@ def test_plan_covers_every_page_once(dev, lens_kind):
     import torch
 
     import mla_decode_attention_amd as mla
-    lens = [0, 1, 64, 65, 5000, 65536, 12345, 3] if lens_kind == "mixed" else _long_batch_lens(300, 41)
+    lens = _plan_lens(lens_kind)
     sl = torch.tensor(lens, dtype=torch.int32, device=dev)
     for s_q, heads in [(1, 16), (2, 16), (1, 128), (2, 128)]:
         ws = torch.zeros(mla.workspace_size(len(lens), s_q, heads), dtype=torch.uint8, device=dev)
@@ -192,11 +206,12 @@ def test_plan_covers_every_page_once(dev, lens_kind):
         pages = [(L + 63) // 64 for L in lens]
         if slots > len(lens):
             chunk = next(c for c in range(1, max(pages) + 2) if sum(-(-p // c) for p in pages) <= slots)
-            assert n_items <= slots and max(sizes) <= chunk
+            assert n_items <= slots and max(sizes, default=0) <= chunk
         else:   # every sequence is one item
             chunk = max(pages)
             assert n_items == sum(p > 0 for p in pages)
-        log(f"plan s_q={s_q} h={heads}: {n_items} items (capacity {cap}), chunk {chunk}, sizes {min(sizes)}..{max(sizes)}")
+        log(f"plan s_q={s_q} h={heads}: {n_items} items (capacity {cap}), chunk {chunk}, "
+            f"sizes {min(sizes, default=0)}..{max(sizes, default=0)}")
 
 
 @pytest.mark.parametrize("heads,s_q,batch", [(16, 1, 300), (16, 2, 300), (128, 1, 140)])
