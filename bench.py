@@ -34,12 +34,24 @@ def log(msg: str) -> None:
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_digest() -> str:
+def source_code_digest(texts) -> str:
+    """sha256 of C++ sources with comments and whitespace removed: an edit of a comment keeps the
+    measurements taken on that code valid, any change of code does not."""
+    import re
     h = hashlib.sha256()
-    for f in ("mla_decode_kernels.h", "mla_decode.hip"):
-        with open(os.path.join(ROOT, "mla_decode_attention_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    for txt in texts:
+        txt = re.sub(r"/\*.*?\*/", " ", txt, flags=re.S)
+        txt = re.sub(r"//[^\n]*", " ", txt)
+        h.update(" ".join(txt.split()).encode())
     return h.hexdigest()[:16]
+
+
+def kernel_source_digest() -> str:
+    texts = []
+    for f in ("mla_decode_kernels.h", "mla_decode.hip"):
+        with open(os.path.join(ROOT, "mla_decode_attention_amd", "csrc", f)) as fh:
+            texts.append(fh.read())
+    return source_code_digest(texts)
 
 
 def measured_traffic(workload: str):

@@ -128,8 +128,8 @@ bool heads_ok(int s_q, int heads)
     return (s_q == 1 || s_q == 2) && (heads == 16 || heads == 32 || heads == 64 || heads == 128);
 }
 
-// Work items the split kernel can take per row group: one per resident workgroup slot, plus one
-// per sequence for the rounding of per-sequence split counts.
+// Work items the split kernel can take per row group: the plan makes at most one per resident
+// workgroup slot, or one per sequence when the batch has at least as many sequences as slots.
 int item_capacity(const DeviceInfo& d, const LaunchGeom& g, int batch)
 {
     int gx = d.num_cu * d.occupancy[g.cfg] / g.row_groups;
