@@ -935,6 +935,10 @@ __global__ void __launch_bounds__(C::THREADS) split_wide_kernel(FwdArgs a)
         constexpr int NU = decltype(nu_tag)::value;
         constexpr int U0 = decltype(u0_tag)::value;
         i32x4 rbuf[NR][NU > 0 ? NU : 1];
+        // kernel arguments the steps use are held in SGPRs from here on: a first use inside the
+        // loop would leave a scalar load pending there, and every LDS wait in the loop would
+        // then have to drain all LDS reads (lgkmcnt(0)) instead of the one it needs
+        asm volatile("" ::"s"(a.num_pages), "s"(a.cache), "s"(a.scale_log2));
         // Loads are issued on every path (a tile past the end reads zeros through an empty
         // resource and is never stored), so the number of loads in flight is the same on every
         // path and each store waits only for its own unit.
@@ -1083,10 +1087,14 @@ __global__ void __launch_bounds__(C::THREADS) split_wide_kernel(FwdArgs a)
 #pragma unroll
                         for (int st = 0; st < 2; ++st)
 #pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                const float v = s[st][i] * a.scale_log2;
-                                s[st][i] = (t0 + 16 * st + 4 * lg + i >= n_vis) ? -__builtin_inff() : v;
-                            }
+                            for (int i = 0; i < 4; ++i) s[st][i] *= a.scale_log2;
+                        if (t0 + C::TT > n_vis) {   // only the tile holding the end of the visible keys
+#pragma unroll
+                            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                                for (int i = 0; i < 4; ++i)
+                                    s[st][i] = (t0 + 16 * st + 4 * lg + i >= n_vis) ? -__builtin_inff() : s[st][i];
+                        }
                         tmax = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                                      fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
                     }
@@ -1161,6 +1169,15 @@ __global__ void __launch_bounds__(C::THREADS) split_wide_kernel(FwdArgs a)
                 const int par = tv & 1;
                 // rows of a block that took a new max in tile tv: rescale their accumulators
                 const i32x4 flags = *reinterpret_cast<const i32x4*>(flag_s + par * 4);
+                // the operand reads go out behind the flags, so the flag check waits for one read
+                const char* pb = pbuf0 + par * C::P_BYTES;
+#pragma unroll
+                for (int rb = 0; rb < NRB; ++rb) pop[rb] = kread(pb + (16 * rb + lr) * C::P_ROW + pchunk);
+#pragma unroll
+                for (int d = 0; d < VD; ++d) {
+                    vlo[d] = vread(vt0 + 32 * d);
+                    vhi[d] = vread(vt0 + 16 * kLdsRow + 32 * d);
+                }
 #pragma unroll
                 for (int rb = 0; rb < NRB; ++rb) {
                     if (__builtin_amdgcn_readfirstlane(flags[rb]) != 0) {
@@ -1171,14 +1188,6 @@ __global__ void __launch_bounds__(C::THREADS) split_wide_kernel(FwdArgs a)
                             __builtin_amdgcn_sched_barrier(0);
                         }
                     }
-                }
-                const char* pb = pbuf0 + par * C::P_BYTES;
-#pragma unroll
-                for (int rb = 0; rb < NRB; ++rb) pop[rb] = kread(pb + (16 * rb + lr) * C::P_ROW + pchunk);
-#pragma unroll
-                for (int d = 0; d < VD; ++d) {
-                    vlo[d] = vread(vt0 + 32 * d);
-                    vhi[d] = vread(vt0 + 16 * kLdsRow + 32 * d);
                 }
             }
 #pragma unroll
