@@ -982,11 +982,21 @@ __global__ void __launch_bounds__(C::THREADS) split_wide_kernel(FwdArgs a)
             if (n_tiles > 1) store_all(1, Idx<1>{});
             load_all(3, Idx<1>{});
         } else {
+            // tiles 0 and 1 go out together (tile 1 waits in a second register set until tile 0
+            // is stored), so the prologue pays one memory round trip for them, not two
+            i32x4 rb1[NU > 0 ? NU : 1];
             load_all(0, Idx<0>{});
+            if constexpr (NU > 0) {
+                const __amdgpu_buffer_rsrc_t r1 = 1 < n_tiles ? tile_rsrc(1) : no_rsrc();
+#pragma unroll
+                for (int k = 0; k < NU; ++k) load_unit(rb1[k], r1, U0 + k);
+            }
             store_all(0, Idx<0>{});
-            load_all(1, Idx<0>{});
-            if (n_tiles > 1) store_all(1, Idx<0>{});
             load_all(2, Idx<0>{});
+            if (n_tiles > 1) {
+#pragma unroll
+                for (int k = 0; k < NU; ++k) store_unit(1, rb1[k], U0 + k);
+            }
         }
         __syncthreads();
         prologue_work();
