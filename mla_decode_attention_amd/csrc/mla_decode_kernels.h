@@ -785,9 +785,10 @@ __global__ void __launch_bounds__(C::THREADS) split_kernel(FwdArgs a)
 }
 
 // =============================================================================================
-// Split kernel, wide form (128 or 256 query rows per sequence: all heads on one GPU).
+// Split kernel, wide form (32 to 256 query rows per sequence; 128 is all heads on one GPU).
 //
-// A work item is taken by `row_groups` workgroups of 64 query rows each.  Their ids are 8 apart
+// A work item is taken by `row_groups` workgroups of 16 NRB query rows each (32 or 64; more
+// rows per sequence take more row groups).  Their ids are 8 apart
 // (id = 8 * row_group + item % 8 within a block of 8 * row_groups ids), so with round-robin
 // dispatch over the 8 XCDs they run together on one XCD and the second read of every KV tile
 // is served by that XCD's L2.
@@ -796,9 +797,10 @@ __global__ void __launch_bounds__(C::THREADS) split_kernel(FwdArgs a)
 //   score waves 0-3: wave w owns query rows 16w..16w+15 (Q^T in registers), computes
 //           S^T = K Q^T for them, keeps their online-softmax statistics and writes P^T (bf16)
 //           and the rescale factors to LDS;
-//   value waves 4-7: wave 4+w owns value dims 128w..128w+127 of all 64 rows and accumulates
-//           O^T += V^T P^T, reading each V^T operand once for the four 16-row blocks.
-// With two waves per SIMD one wave's MFMAs run while the other waits or does vector work.
+//   value waves 4-7: wave 4+w owns value dims 128w..128w+127 of all the group's rows and
+//           accumulates O^T += V^T P^T, reading each V^T operand once for all 16-row blocks.
+// With 32 rows, score waves 2-3 have no rows and only stage tiles.  With two waves per SIMD
+// one wave's MFMAs run while the other waits on LDS reads or tile data.
 // Both roles stream the KV tiles HBM -> VGPR -> LDS (each wave a fixed share of every tile).
 // Step t: score waves score tile t+1 and run the softmax of tile t; value waves accumulate
 // tile t-1; one barrier per step.  LDS holds four tile stages: t-1 (value), t (waiting for its
