@@ -53,6 +53,37 @@ def test_ragged_lengths_all_row_configs(dev, heads, s_q, causal):
     full_parity(case, dev)
 
 
+def _sweep_params(n=16, seed=4242):
+    """Seeded shapes for the sweep: head count, query tokens, causal flag, batch, a length mix
+    (wide random, page multiples +-1, tiny) and the softmax scale (including 0 and a negative)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        heads = int(rng.choice([16, 32, 64, 128]))
+        s_q = int(rng.integers(1, 3))
+        causal = bool(rng.integers(0, 2))
+        batch = int(rng.integers(1, 5 if heads >= 64 else 13))
+        kind = int(rng.integers(0, 3))
+        top = 3000 if heads >= 64 else 6000
+        if kind == 0:
+            lens = rng.integers(0, top, size=batch)
+        elif kind == 1:
+            lens = np.clip(64 * rng.integers(0, top // 64, size=batch) + rng.integers(-1, 2, size=batch), 0, None)
+        else:
+            lens = rng.integers(0, 130, size=batch)
+        scale = float(rng.choice([1.0 / np.sqrt(192.0), 0.02, 0.25, -0.08, 0.0]))
+        out.append(pytest.param(heads, s_q, causal, [int(x) for x in lens], scale, 5000 + i, id=f"sweep{i}"))
+    return out
+
+
+@pytest.mark.parametrize("heads,s_q,causal,lens,scale,seed", _sweep_params())
+def test_seeded_shape_sweep(dev, heads, s_q, causal, lens, scale, seed):
+    case = make_case(f"sweep_h{heads}_sq{s_q}", batch=len(lens), s_q=s_q, heads=heads, seqlen=lens, seed=seed,
+                     causal=causal, softmax_scale=scale, pool_pages=sum((L + 63) // 64 for L in lens) + 3,
+                     table_slack=2)
+    full_parity(case, dev, f"{case.name} scale={scale:.4g}")
+
+
 def test_empty_and_single_key_sequences(dev):
     case = make_case("empty_mix", batch=5, s_q=2, heads=16, seqlen=[0, 1, 2, 0, 70], seed=32, causal=True)
     full_parity(case, dev)
