@@ -30,6 +30,41 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 
 
+def read_probe_gbs(dev, stream, reps: int = 10):
+    """Streaming-read rate of this GPU: a plain kernel (libmla_read_probe.so, built beside the
+    decode library) reads 1 GiB once per launch; GB/s of bytes read.  None if it is not built."""
+    import ctypes
+
+    import torch
+
+    import mla_decode_attention_amd as mla
+    path = os.path.join(os.path.dirname(mla.LIB_PATH), "libmla_read_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.mla_read_probe_out_words.restype = ctypes.c_int
+    lib.mla_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p, ctypes.c_longlong,
+                                   ctypes.c_void_p]
+    words = lib.mla_read_probe_out_words()
+    if words <= 0:
+        return None
+    buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    out = torch.empty(words, dtype=torch.int32, device=dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    run = lambda: lib.mla_read_probe(buf.data_ptr(), buf.numel(), out.data_ptr(), words, sp)
+    for _ in range(3):
+        if run() != 0:
+            return None
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    chunk = 18 * 1024
+    return (buf.numel() // chunk) * chunk * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
 def log(msg: str) -> None:
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
@@ -375,6 +410,9 @@ def main() -> int:
     copy_gbs = 2 * src.numel() * 4 * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del src, dst
     log(f"device copy probe: {copy_gbs:.0f} GB/s (read + write)")
+    read_gbs = read_probe_gbs(dev, stream)
+    if read_gbs is not None:
+        log(f"streaming-read probe: {read_gbs:.0f} GB/s")
 
     flushed = None
     if args.flush_mib > 0:
@@ -471,7 +509,10 @@ def main() -> int:
                      "traffic": measured_traffic(name), "avg_launch_us": round(split_avg_ms * 1e3, 2),
                      "algorithmic_bytes_per_launch": kv_q_bytes,
                      "mfma_frac": round(split_flops / (split_avg_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "copy_probe_GB/s": round(copy_gbs, 1), "frac_of_copy_probe": round(split_gbs / copy_gbs, 4)},
+                     "median_launch_us": round(float(np.median(split_ms)) * 1e3, 2),
+                     "copy_probe_GB/s": round(copy_gbs, 1), "frac_of_copy_probe": round(split_gbs / copy_gbs, 4),
+                     "read_probe_GB/s": None if read_gbs is None else round(read_gbs, 1),
+                     "frac_of_read_probe": None if read_gbs is None else round(split_gbs / read_gbs, 4)},
         "cpu_baseline": cpu,
         "parity_vs_oracle": parity,
         "extras": extras,

@@ -39,5 +39,22 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None, out: str 
     return out
 
 
+PROBE_LIB = os.path.join(PKG, "libmla_read_probe.so")
+
+
+def build_read_probe(verbose: bool = False) -> str:
+    """The streaming-read probe bench.py times beside the decode kernels (its own library)."""
+    tmp = f"{PROBE_LIB}.tmp{os.getpid()}"
+    cmd = [HIPCC, *FLAGS, os.path.join(CSRC, "read_probe.hip"), "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if "packed-fp32-ops" not in l)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msgs}")
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
