@@ -148,6 +148,13 @@ def cpu_baseline(case, o_gpu, lse_gpu, n_seqs: int, threads: int, min_seconds: f
         dt += time.perf_counter() - t0
         reps += 1
     sample_bytes = W.algorithmic_bytes(case.seqlens[:n_seqs], n_seqs, case.s_q, case.heads)
+    # per-core figure: one thread over the first sequence's rows
+    rows1 = np.arange(case.s_q * case.heads, dtype=np.int64)
+    t0 = time.perf_counter()
+    oracle.mla_decode(case.q, case.cache, case.block_table, case.seqlens, case.softmax_scale, case.causal,
+                      rows=rows1, threads=1)
+    dt1 = time.perf_counter() - t0
+    bytes1 = W.algorithmic_bytes(case.seqlens[:1], 1, case.s_q, case.heads)
     err = np.abs(o_gpu.reshape(case.rows, -1)[rows] - ro)
     rl_ok = np.isfinite(rl)
     parity = dict(rows=int(rows.size), o_maxabs=float(err.max()), o_rmse=float(np.sqrt(np.mean(err ** 2))),
@@ -157,7 +164,10 @@ def cpu_baseline(case, o_gpu, lse_gpu, n_seqs: int, threads: int, min_seconds: f
                 sample=f"{n_seqs} of {case.batch} sequences, all {case.s_q * case.heads} query rows each "
                        f"({rows.size} rows, {sample_bytes / 1e6:.1f} MB algorithmic), run {reps}x, "
                        f"fp64 C oracle (OpenMP)",
-                seconds=round(dt, 2), cpu_model=_cpu_model(), host_cpus=os.cpu_count()), parity
+                seconds=round(dt, 2), cpu_model=_cpu_model(), host_cpus=os.cpu_count(),
+                per_core_value=bytes1 / dt1 / 1e12,
+                per_core_sample=f"1 thread, 1 sequence ({rows1.size} rows, {bytes1 / 1e6:.1f} MB algorithmic), "
+                                f"{dt1:.2f} s"), parity
 
 
 def _cpu_model() -> str:
