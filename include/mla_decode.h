@@ -45,6 +45,7 @@ extern "C" {
 #define MLA_DECODE_D_K 576      /* latent (512) + shared RoPE key (64) */
 #define MLA_DECODE_D_V 512      /* value = first 512 dims of a cache row */
 #define MLA_DECODE_PAGE_SIZE 64 /* tokens per cache page */
+#define MLA_DECODE_MAX_BATCH (1 << 20) /* sequences per call (decode, GQA decode, cache append) */
 
 typedef enum mla_status {
     MLA_OK = 0,
@@ -58,7 +59,7 @@ typedef enum mla_status {
 /*
  * Bytes of device workspace that mla_decode_plan / mla_decode_fwd need for this
  * shape on the current device (the split count scales with its compute units).
- *   batch      >= 1 sequences
+ *   batch      1 .. MLA_DECODE_MAX_BATCH sequences (larger: MLA_ERR_INVALID_ARG)
  *   s_q        1 or 2 query tokens per sequence
  *   num_heads  16, 32, 64 or 128
  *   bytes      out: required size
@@ -232,7 +233,7 @@ int mla_sparse_decode_fwd(const void *q, const void *kv_cache, const int32_t *bl
  *   k_rope     bf16 [batch][s_q][64], device, before rotation
  *   q          bf16 [batch][s_q][num_heads][576], device, dims 512..575 rotated in place
  *   kv_cache   bf16 [num_pages][64][576], device, one row written per new token
- *   block_table, bt_stride, seqlens, num_pages, page_size: as for mla_decode_fwd
+ *   block_table, bt_stride, seqlens, batch, num_pages, page_size: as for mla_decode_fwd
  *   rope_base  finite, > 1 (e.g. 10000)
  * Device-side input errors do not fault: a token whose pos is negative, whose L_b exceeds
  * 64*bt_stride or whose page is outside [0, num_pages) writes no cache row and gets NaN in the

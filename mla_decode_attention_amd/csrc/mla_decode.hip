@@ -123,6 +123,8 @@ int device_info(const DeviceInfo** out)
     return d.status;
 }
 
+bool batch_ok(int batch) { return batch >= 1 && batch <= MLA_DECODE_MAX_BATCH; }
+
 bool heads_ok(int s_q, int heads)
 {
     return (s_q == 1 || s_q == 2) && (heads == 16 || heads == 32 || heads == 64 || heads == 128);
@@ -151,7 +153,7 @@ extern "C" {
 
 int mla_decode_workspace_size(int batch, int s_q, int num_heads, size_t* bytes)
 {
-    if (!bytes || batch < 1) return MLA_ERR_INVALID_ARG;
+    if (!bytes || !batch_ok(batch)) return MLA_ERR_INVALID_ARG;
     if (!heads_ok(s_q, num_heads)) return MLA_ERR_UNSUPPORTED;
     const DeviceInfo* d = nullptr;
     const int st = device_info(&d);
@@ -165,7 +167,7 @@ int mla_decode_workspace_size(int batch, int s_q, int num_heads, size_t* bytes)
 int mla_decode_plan(const int32_t* seqlens, int batch, int s_q, int num_heads, void* workspace,
                     size_t workspace_bytes, void* stream)
 {
-    if (!seqlens || !workspace || batch < 1) return MLA_ERR_INVALID_ARG;
+    if (!seqlens || !workspace || !batch_ok(batch)) return MLA_ERR_INVALID_ARG;
     if (!aligned(workspace, 256) || !aligned(seqlens, 4)) return MLA_ERR_INVALID_ARG;
     if (!heads_ok(s_q, num_heads)) return MLA_ERR_UNSUPPORTED;
     const DeviceInfo* d = nullptr;
@@ -190,7 +192,7 @@ int prepare_fwd(const void* q, const void* kv_cache, const int32_t* block_table,
     if (!seqlens || !workspace) return MLA_ERR_INVALID_ARG;
     if (need_inputs && (!q || !kv_cache || !block_table)) return MLA_ERR_INVALID_ARG;
     if (need_outputs && (!out || !lse)) return MLA_ERR_INVALID_ARG;
-    if (batch < 1 || bt_stride < 1) return MLA_ERR_INVALID_ARG;
+    if (!batch_ok(batch) || bt_stride < 1) return MLA_ERR_INVALID_ARG;
     if (need_inputs && num_pages < 1) return MLA_ERR_INVALID_ARG;
     if (need_inputs && (!std::isfinite(softmax_scale) || (causal != 0 && causal != 1))) return MLA_ERR_INVALID_ARG;
     if (!aligned(workspace, 256) || !aligned(seqlens, 4)) return MLA_ERR_INVALID_ARG;
@@ -293,7 +295,7 @@ int mla_cache_append_rope(const void* kv_latent, const void* k_rope, void* q, vo
                           int num_heads, int num_pages, int page_size, float rope_base, void* stream)
 {
     if (!kv_latent || !k_rope || !q || !kv_cache || !block_table || !seqlens) return MLA_ERR_INVALID_ARG;
-    if (batch < 1 || bt_stride < 1 || num_pages < 1) return MLA_ERR_INVALID_ARG;
+    if (!batch_ok(batch) || bt_stride < 1 || num_pages < 1) return MLA_ERR_INVALID_ARG;
     if (!std::isfinite(rope_base) || !(rope_base > 1.f)) return MLA_ERR_INVALID_ARG;
     if (!aligned(kv_latent, 16) || !aligned(k_rope, 4) || !aligned(q, 4) || !aligned(kv_cache, 16) ||
         !aligned(block_table, 4) || !aligned(seqlens, 4))
@@ -492,7 +494,7 @@ namespace {
 
 int gqa_geom(int batch, int s_q, int num_heads, LaunchGeom* g)
 {
-    if (batch < 1) return MLA_ERR_INVALID_ARG;
+    if (!batch_ok(batch)) return MLA_ERR_INVALID_ARG;
     if ((s_q != 1 && s_q != 2) || num_heads != kGqaHeads) return MLA_ERR_UNSUPPORTED;
     *g = s_q == 1 ? LaunchGeom{kG1, 1, kGqaThreads, CfgG1::LDS_BYTES} : LaunchGeom{kG2, 1, kGqaThreads, CfgG2::LDS_BYTES};
     return MLA_OK;

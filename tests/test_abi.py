@@ -47,6 +47,7 @@ def test_header_constants_match_binding():
     assert re.search(r"#define MLA_DECODE_D_K 576\b", text)
     assert re.search(r"#define MLA_DECODE_D_V 512\b", text)
     assert re.search(r"#define MLA_DECODE_PAGE_SIZE 64\b", text)
+    assert re.search(r"#define MLA_DECODE_MAX_BATCH \(1 << 20\)", text)
     for code, name in mla.STATUS.items():
         assert re.search(rf"{name}\s*=\s*{code}\b", text), name
 
@@ -67,7 +68,8 @@ def _fwd(L, **kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(q=0), -1), (dict(kv=0), -1), (dict(bt=0), -1), (dict(sl=0), -1), (dict(ws=0), -1),
-    (dict(out=0), -1), (dict(lse=0), -1), (dict(batch=0), -1), (dict(batch=-3), -1), (dict(bt_stride=0), -1),
+    (dict(out=0), -1), (dict(lse=0), -1), (dict(batch=0), -1), (dict(batch=-3), -1), (dict(batch=(1 << 20) + 1), -1),
+    (dict(bt_stride=0), -1),
     (dict(num_pages=0), -1), (dict(scale=float("nan")), -1), (dict(scale=float("inf")), -1),
     (dict(causal=2), -1), (dict(q=FAKE + 8), -1), (dict(kv=FAKE + 2), -1), (dict(ws=FAKE + 16), -1),
     (dict(heads=8), -2), (dict(heads=24), -2), (dict(heads=256), -2), (dict(s_q=3), -2), (dict(s_q=0), -2),
@@ -81,6 +83,7 @@ def test_plan_argument_errors(L):
     ws = P(FAKE)
     assert L.mla_decode_plan(None, 1, 1, 16, ws, 1 << 20, None) == -1
     assert L.mla_decode_plan(P(FAKE), 0, 1, 16, ws, 1 << 20, None) == -1
+    assert L.mla_decode_plan(P(FAKE), (1 << 20) + 1, 1, 16, ws, 1 << 20, None) == -1
     assert L.mla_decode_plan(P(FAKE), 1, 1, 16, None, 1 << 20, None) == -1
     assert L.mla_decode_plan(P(FAKE), 1, 1, 16, P(FAKE + 4), 1 << 20, None) == -1
     assert L.mla_decode_plan(P(FAKE), 1, 3, 16, ws, 1 << 20, None) == -2
@@ -91,6 +94,7 @@ def test_workspace_size_argument_errors(L):
     n = ctypes.c_size_t(0)
     assert L.mla_decode_workspace_size(1, 1, 16, None) == -1
     assert L.mla_decode_workspace_size(0, 1, 16, ctypes.byref(n)) == -1
+    assert L.mla_decode_workspace_size((1 << 20) + 1, 1, 16, ctypes.byref(n)) == -1
     assert L.mla_decode_workspace_size(1, 2, 48, ctypes.byref(n)) == -2
 
 
@@ -105,7 +109,8 @@ def _append(L, **kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(lat=0), -1), (dict(rope=0), -1), (dict(q=0), -1), (dict(kv=0), -1), (dict(bt=0), -1), (dict(sl=0), -1),
-    (dict(batch=0), -1), (dict(bt_stride=0), -1), (dict(num_pages=0), -1), (dict(base=1.0), -1),
+    (dict(batch=0), -1), (dict(batch=(1 << 20) + 1), -1), (dict(bt_stride=0), -1), (dict(num_pages=0), -1),
+    (dict(base=1.0), -1),
     (dict(base=float("nan")), -1), (dict(base=float("inf")), -1), (dict(lat=FAKE + 8), -1), (dict(q=FAKE + 2), -1),
     (dict(heads=8), -2), (dict(s_q=3), -2), (dict(page_size=128), -2),
 ])
@@ -163,7 +168,8 @@ def test_gqa_argument_errors(L):
     call = lambda a: L.mla_gqa_decode_fwd(P(a["q"]), P(a["kv"]), P(a["bt"]), a["bs"], P(a["sl"]), a["b"], a["s_q"],
                                            a["h"], a["np_"], a["ps"], ctypes.c_float(a["sc"]), a["c"], P(a["ws"]),
                                            a["wsb"], P(a["out"]), P(a["lse"]), None)
-    for kw, code in [(dict(q=0), -1), (dict(kv=0), -1), (dict(b=0), -1), (dict(c=3), -1), (dict(sc=float("inf")), -1),
+    for kw, code in [(dict(q=0), -1), (dict(kv=0), -1), (dict(b=0), -1), (dict(b=(1 << 20) + 1), -1), (dict(c=3), -1),
+                     (dict(sc=float("inf")), -1),
                      (dict(q=FAKE + 2), -1), (dict(h=32), -2), (dict(s_q=3), -2), (dict(ps=32), -2)]:
         assert call(args(**kw)) == code, kw
     assert L.mla_gqa_decode_workspace_size(1, 1, 16, None) == -1
