@@ -87,7 +87,8 @@ enum HeaderField { kHMagic = 0, kHBatch, kHSq, kHHeads, kHItems, kHCapacity, kHR
 // =============================================================================================
 constexpr int kPlanThreads = 1024;
 
-__device__ inline int pages_of(int L) { return L <= 0 ? 0 : (L + kPage - 1) / kPage; }
+// no L + 63 (which overflows int for L within 63 of INT_MAX)
+__device__ inline int pages_of(int L) { return L <= 0 ? 0 : L / kPage + (L % kPage != 0 ? 1 : 0); }
 
 // uniform_len >= 0: every sequence has that length and `seqlens` is not read (sparse decode: each
 // query token is a sequence of top-k index slots)
@@ -433,7 +434,7 @@ __global__ void __launch_bounds__(C::THREADS) split_kernel(FwdArgs a)
     const bool bad_seq = (L != plan_L) | (L < 0) | (Lc < 0) | ((long long)Lc > (long long)kPage * a.bt_stride);
     const int n_vis = (!SPARSE && a.causal) ? min(max(L - a.s_q + 1 + qi, 0), L) : L;
     const int tok_begin = it[1] * kPage;
-    const int tok_end = min(it[2] * kPage, L);
+    const int tok_end = (int)min((long long)it[2] * kPage, (long long)L);   // it[2] * 64 may reach 2^31
     const int n_tiles = bad_seq ? 0 : (tok_end - tok_begin + C::TT - 1) / C::TT;
     const int n_it = (n_tiles + C::NG - 1) / C::NG;
 
@@ -876,7 +877,7 @@ __global__ void __launch_bounds__(C::THREADS) split_wide_kernel(FwdArgs a)
     const bool bad_seq = (L != plan_L) | (L < 0) | ((long long)L > (long long)kPage * a.bt_stride);
     const int n_vis = a.causal ? min(max(L - a.s_q + 1 + qi, 0), L) : L;
     const int tok_begin = it[1] * kPage;
-    const int tok_end = min(it[2] * kPage, L);
+    const int tok_end = (int)min((long long)it[2] * kPage, (long long)L);   // it[2] * 64 may reach 2^31
     const int n_tiles = bad_seq ? 0 : (tok_end - tok_begin + C::TT - 1) / C::TT;
 
     // ---- tile staging, shared by both roles: the waves w and w + 4 move 8-row group w of every

@@ -80,7 +80,7 @@ __global__ void __launch_bounds__(kGqaThreads) gqa_split_kernel(FwdArgs a)
     // (no early exit: a branch here would make the loads above wait one after another).
     const bool bad_seq = (L != plan_L) | (L < 0) | ((long long)L > (long long)kPage * a.bt_stride);
     const int tok_begin = it[1] * kPage;
-    const int tok_end = min(it[2] * kPage, L);
+    const int tok_end = (int)min((long long)it[2] * kPage, (long long)L);   // it[2] * 64 may reach 2^31
     const int n_tiles = bad_seq ? 0 : (tok_end - tok_begin + kGqaTT - 1) / kGqaTT;
     const int n_it = (n_tiles + kGqaWaves - 1) / kGqaWaves;
     int n_vis[NRB];

@@ -186,11 +186,13 @@ def _plan_lens(kind):
         "many_tiny": lambda: [int(x) for x in rng.integers(1, 65, 200)],
         "uneven_like_mtp": lambda: [int(x) for x in rng.integers(8192, 16385, 16)],
         "batch_near_slots": lambda: [int(x) for x in rng.integers(0, 5000, 120)],
+        # the plan reads only the lengths: page counts near 2^25 (INT_MAX tokens) must not overflow
+        "near_int_max": lambda: [2 ** 31 - 1, 2 ** 31 - 64, 5, 0],
     }[kind]()
 
 
 @pytest.mark.parametrize("lens_kind", ["mixed", "batch_beyond_slots", "all_empty", "one_huge", "many_tiny",
-                                       "uneven_like_mtp", "batch_near_slots"])
+                                       "uneven_like_mtp", "batch_near_slots", "near_int_max"])
 def test_plan_covers_every_page_once(dev, lens_kind):
     """Read the plan back: items tile each sequence's pages exactly once, in balanced chunks of the
     smallest size that fits one wave of split workgroups (one item per sequence once the batch
@@ -228,15 +230,26 @@ def test_plan_covers_every_page_once(dev, lens_kind):
             pages = (L + 63) // 64
             assert (its[:, 0] == b).all()
             assert its[:, 3].tolist() == list(range(len(its)))
-            covered = [p for it in its for p in range(it[1], it[2])]
-            assert covered == list(range(pages)), (b, L)
+            # the item ranges tile [0, pages) in order, each non-empty
+            if pages == 0:
+                assert len(its) == 0, (b, L)
+            else:
+                assert its[0, 1] == 0 and its[-1, 2] == pages, (b, L)
+                assert (its[1:, 1] == its[:-1, 2]).all() and (its[:, 2] > its[:, 1]).all(), (b, L)
             sizes += (its[:, 2] - its[:, 1]).tolist()
         # the chunk is the smallest page count whose per-sequence split counts fit the
         # cap - batch workgroup slots (one wave of split workgroups)
         slots = cap - len(lens)
         pages = [(L + 63) // 64 for L in lens]
         if slots > len(lens):
-            chunk = next(c for c in range(1, max(pages) + 2) if sum(-(-p // c) for p in pages) <= slots)
+            lo, hi = 1, max(pages) + 1   # smallest c with sum ceil(p / c) <= slots (bisection: it is monotone)
+            while lo < hi:
+                mid = (lo + hi) // 2
+                if sum(-(-p // mid) for p in pages) <= slots:
+                    hi = mid
+                else:
+                    lo = mid + 1
+            chunk = lo
             assert n_items <= slots and max(sizes, default=0) <= chunk
         else:   # every sequence is one item
             chunk = max(pages)
