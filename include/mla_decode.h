@@ -203,6 +203,8 @@ int mla_unabsorb_o(const void *o_latent, const void *w_uv, int batch, int s_q, i
  *   indices    int32 [batch][s_q][topk], device: logical token positions of sequence b (its row
  *              is page block_table[b][j / 64], slot j % 64); -1 marks an unused slot; a position
  *              listed twice counts as two keys
+ *   num_pages  1 .. 2^25 (cache rows are addressed with 32-bit row ids here; 2^25 pages are
+ *              2.5 TB, more than one GPU holds)
  *   other arguments as for mla_decode_fwd (there is no causal flag: the lists decide)
  * Device-side input errors do not fault: a token with an index outside [0, L_b), or whose row
  * lies on a page outside [0, num_pages), or whose sequence has L_b outside [0, 64*bt_stride],

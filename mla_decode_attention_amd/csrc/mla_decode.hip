@@ -375,7 +375,9 @@ int mla_sparse_decode_fwd(const void* q, const void* kv_cache, const int32_t* bl
 {
     if (!q || !kv_cache || !block_table || !seqlens || !indices || !workspace || !out || !lse)
         return MLA_ERR_INVALID_ARG;
-    if (bt_stride < 1 || num_pages < 1 || !std::isfinite(softmax_scale)) return MLA_ERR_INVALID_ARG;
+    // the gather forms 32-bit cache row ids (page * 64 + slot)
+    if (bt_stride < 1 || num_pages < 1 || num_pages > (1 << 25) || !std::isfinite(softmax_scale))
+        return MLA_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(block_table, 4) || !aligned(seqlens, 4) ||
         !aligned(indices, 4) || !aligned(workspace, 256) || !aligned(out, 8) || !aligned(lse, 4))
         return MLA_ERR_INVALID_ARG;

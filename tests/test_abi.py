@@ -130,6 +130,7 @@ def _sparse_fwd(L, **kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(q=0), -1), (dict(ind=0), -1), (dict(ws=0), -1), (dict(out=0), -1), (dict(batch=0), -1), (dict(topk=0), -1),
+    (dict(num_pages=(1 << 25) + 1), -1),
     (dict(bt_stride=0), -1), (dict(num_pages=0), -1), (dict(scale=float("nan")), -1), (dict(ind=FAKE + 2), -1),
     (dict(ws=FAKE + 64), -1), (dict(heads=32), -2), (dict(heads=128), -2), (dict(s_q=3), -2), (dict(page_size=16), -2),
 ])
