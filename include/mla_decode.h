@@ -97,7 +97,7 @@ int mla_decode_plan(const int32_t *seqlens, int batch, int s_q, int num_heads, v
  *   bt_stride    int32 entries per block_table row (>= 1)
  *   seqlens      int32 [batch], the same values the plan was made from
  *   num_pages    pages in kv_cache (>= 1); page_size must be 64
- *   softmax_scale  finite scale applied to q.k (e.g. 1/sqrt(192))
+ *   softmax_scale  scale applied to q.k (e.g. 1/sqrt(192)); it and scale * log2(e) must be finite
  *   causal       0: every query token sees all L_b keys; 1: bottom-right causal
  *   out          bf16 [batch][s_q][num_heads][512], written (round to nearest even)
  *   lse          fp32 [batch][s_q][num_heads], natural-log LSE, written

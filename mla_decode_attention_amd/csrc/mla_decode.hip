@@ -194,7 +194,8 @@ int prepare_fwd(const void* q, const void* kv_cache, const int32_t* block_table,
     if (need_outputs && (!out || !lse)) return MLA_ERR_INVALID_ARG;
     if (!batch_ok(batch) || bt_stride < 1) return MLA_ERR_INVALID_ARG;
     if (need_inputs && num_pages < 1) return MLA_ERR_INVALID_ARG;
-    if (need_inputs && (!std::isfinite(softmax_scale) || (causal != 0 && causal != 1))) return MLA_ERR_INVALID_ARG;
+    if (need_inputs && (!std::isfinite(softmax_scale * kLog2e) || (causal != 0 && causal != 1)))
+        return MLA_ERR_INVALID_ARG;
     if (!aligned(workspace, 256) || !aligned(seqlens, 4)) return MLA_ERR_INVALID_ARG;
     if (need_inputs && (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(block_table, 4)))
         return MLA_ERR_INVALID_ARG;
@@ -376,7 +377,7 @@ int mla_sparse_decode_fwd(const void* q, const void* kv_cache, const int32_t* bl
     if (!q || !kv_cache || !block_table || !seqlens || !indices || !workspace || !out || !lse)
         return MLA_ERR_INVALID_ARG;
     // the gather forms 32-bit cache row ids (page * 64 + slot)
-    if (bt_stride < 1 || num_pages < 1 || num_pages > (1 << 25) || !std::isfinite(softmax_scale))
+    if (bt_stride < 1 || num_pages < 1 || num_pages > (1 << 25) || !std::isfinite(softmax_scale * kLog2e))
         return MLA_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(block_table, 4) || !aligned(seqlens, 4) ||
         !aligned(indices, 4) || !aligned(workspace, 256) || !aligned(out, 8) || !aligned(lse, 4))
@@ -541,7 +542,7 @@ int mla_gqa_decode_fwd(const void* q, const void* kv_cache, const int32_t* block
                        void* stream)
 {
     if (!q || !kv_cache || !block_table || !seqlens || !workspace || !out || !lse) return MLA_ERR_INVALID_ARG;
-    if (bt_stride < 1 || num_pages < 1 || !std::isfinite(softmax_scale) || (causal != 0 && causal != 1))
+    if (bt_stride < 1 || num_pages < 1 || !std::isfinite(softmax_scale * kLog2e) || (causal != 0 && causal != 1))
         return MLA_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(block_table, 4) || !aligned(seqlens, 4) ||
         !aligned(workspace, 256) || !aligned(out, 2) || !aligned(lse, 4))

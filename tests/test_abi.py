@@ -70,7 +70,7 @@ def _fwd(L, **kw):
     (dict(q=0), -1), (dict(kv=0), -1), (dict(bt=0), -1), (dict(sl=0), -1), (dict(ws=0), -1),
     (dict(out=0), -1), (dict(lse=0), -1), (dict(batch=0), -1), (dict(batch=-3), -1), (dict(batch=(1 << 20) + 1), -1),
     (dict(bt_stride=0), -1),
-    (dict(num_pages=0), -1), (dict(scale=float("nan")), -1), (dict(scale=float("inf")), -1),
+    (dict(num_pages=0), -1), (dict(scale=float("nan")), -1), (dict(scale=float("inf")), -1), (dict(scale=3e38), -1),
     (dict(causal=2), -1), (dict(q=FAKE + 8), -1), (dict(kv=FAKE + 2), -1), (dict(ws=FAKE + 16), -1),
     (dict(heads=8), -2), (dict(heads=24), -2), (dict(heads=256), -2), (dict(s_q=3), -2), (dict(s_q=0), -2),
     (dict(page_size=32), -2),
