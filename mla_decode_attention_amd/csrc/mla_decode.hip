@@ -419,7 +419,7 @@ int mla_sparse_decode_fwd(const void* q, const void* kv_cache, const int32_t* bl
     // the combine checks each token's length against the plan's copy of it and the table width
     FwdArgs c = a;
     c.seqlens = reinterpret_cast<const int32_t*>(a.ws + lay.seqlens);
-    c.bt_stride = (topk + kPage - 1) / kPage;
+    c.bt_stride = topk / kPage + (topk % kPage != 0 ? 1 : 0);   // no topk + 63 (overflow near INT_MAX)
     return launch_combine(c, s);
 }
 
