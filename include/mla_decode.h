@@ -61,7 +61,7 @@ typedef enum mla_status {
  * shape on the current device (the split count scales with its compute units).
  *   batch      1 .. MLA_DECODE_MAX_BATCH sequences (larger: MLA_ERR_INVALID_ARG)
  *   s_q        1 or 2 query tokens per sequence
- *   num_heads  16, 32, 64 or 128
+ *   num_heads  a multiple of 16 from 16 to 128 (one GPU's share of a model's heads)
  *   bytes      out: required size
  * Returns MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED or MLA_ERR_NO_DEVICE.
  */
@@ -93,7 +93,8 @@ int mla_decode_plan(const int32_t *seqlens, int batch, int s_q, int num_heads, v
  *   kv_cache     bf16 [num_pages][64][576], contiguous paged latent cache
  *   block_table  int32 [batch][bt_stride]: entry p of row b is the pool page
  *                holding tokens 64p .. 64p+63 of sequence b; entries at or past
- *                ceil(L_b / 64) are never read
+ *                ceil(L_b / 64) are not used (the kernels read the row in windows of up
+ *                to 64 entries, always inside its bt_stride entries)
  *   bt_stride    int32 entries per block_table row (>= 1)
  *   seqlens      int32 [batch], the same values the plan was made from
  *   num_pages    pages in kv_cache (>= 1); page_size must be 64

@@ -13,6 +13,7 @@
 #include "mla_append_kernels.h"
 #include "mla_gqa_kernels.h"
 #include "mla_decode_kernels.h"
+#include "mla_sv_kernel.h"
 
 namespace {
 
@@ -28,11 +29,15 @@ using CfgR16 = SplitCfg<4, 1, 1, 16, 1, 1>;    // 4 independent waves, one 18 Ki
 using CfgW32 = WideCfg<1, 5, 2>;               // 32 rows per workgroup
 using CfgW64 = WideCfg<1, 5, 4>;               // 64 rows per workgroup (row groups of 64 above)
 
+//                 32-row blocks
+using CfgSV1 = SvCfg<1>;                       // 32 rows per workgroup
+using CfgSV2 = SvCfg<2>;                       // 64 rows per workgroup (row groups of 64 above)
+
 using CfgG1 = GqaCfg<1>;                       // GQA path, one query token per step
 using CfgG2 = GqaCfg<2>;                       // GQA path, two query tokens per step
 
 // kS16: sparse (gathered-row) form of kR16; kG1 / kG2: GQA path
-enum CfgId { kR16 = 0, kW32, kW64, kS16, kG1, kG2, kNumCfg };
+enum CfgId { kR16 = 0, kW32, kW64, kS16, kG1, kG2, kSV1, kSV2, kNumCfg };
 
 struct LaunchGeom {
     CfgId cfg;
@@ -44,14 +49,17 @@ struct LaunchGeom {
 bool geom_for(int s_q, int heads, LaunchGeom* g)
 {
     const int rows = s_q * heads;
-    switch (rows) {
-    case 16: *g = {kR16, 1, CfgR16::THREADS, CfgR16::LDS_BYTES}; return true;
-    case 32: *g = {kW32, 1, CfgW32::THREADS, CfgW32::LDS_BYTES}; return true;
-    case 64: *g = {kW64, 1, CfgW64::THREADS, CfgW64::LDS_BYTES}; return true;
-    case 128: *g = {kW64, 2, CfgW64::THREADS, CfgW64::LDS_BYTES}; return true;
-    case 256: *g = {kW64, 4, CfgW64::THREADS, CfgW64::LDS_BYTES}; return true;
-    default: return false;
+    if (rows == 16) {
+        *g = {kR16, 1, CfgR16::THREADS, CfgR16::LDS_BYTES};
+        return true;
     }
+    if (rows % 16 != 0 || rows > 256) return false;
+    if (rows == 32) {
+        *g = {kSV1, 1, CfgSV1::THREADS, CfgSV1::LDS_BYTES};
+        return true;
+    }
+    *g = {kSV2, (rows + 63) / 64, CfgSV2::THREADS, CfgSV2::LDS_BYTES};
+    return true;
 }
 
 const void* split_fn(CfgId c)
@@ -62,6 +70,8 @@ const void* split_fn(CfgId c)
     case kS16: return reinterpret_cast<const void*>(&split_kernel<CfgR16, true>);
     case kG1: return reinterpret_cast<const void*>(&gqa_split_kernel<CfgG1>);
     case kG2: return reinterpret_cast<const void*>(&gqa_split_kernel<CfgG2>);
+    case kSV1: return reinterpret_cast<const void*>(&split_sv_kernel<CfgSV1>);
+    case kSV2: return reinterpret_cast<const void*>(&split_sv_kernel<CfgSV2>);
     default: return reinterpret_cast<const void*>(&split_wide_kernel<CfgW64>);
     }
 }
@@ -102,9 +112,11 @@ int device_info(const DeviceInfo** out)
         } else {
             d.num_cu = prop.multiProcessorCount;
             static const int threads[kNumCfg] = {CfgR16::THREADS, CfgW32::THREADS, CfgW64::THREADS,
-                                                 CfgR16::THREADS, kGqaThreads,     kGqaThreads};
+                                                 CfgR16::THREADS, kGqaThreads,     kGqaThreads,
+                                                 CfgSV1::THREADS, CfgSV2::THREADS};
             static const int lds[kNumCfg] = {CfgR16::LDS_BYTES, CfgW32::LDS_BYTES, CfgW64::LDS_BYTES,
-                                             CfgR16::LDS_BYTES, CfgG1::LDS_BYTES, CfgG2::LDS_BYTES};
+                                             CfgR16::LDS_BYTES, CfgG1::LDS_BYTES, CfgG2::LDS_BYTES,
+                                             CfgSV1::LDS_BYTES, CfgSV2::LDS_BYTES};
             for (int c = 0; c < kNumCfg; ++c) {
                 const void* fn = split_fn(static_cast<CfgId>(c));
                 int occ = 0;
@@ -127,7 +139,7 @@ bool batch_ok(int batch) { return batch >= 1 && batch <= MLA_DECODE_MAX_BATCH; }
 
 bool heads_ok(int s_q, int heads)
 {
-    return (s_q == 1 || s_q == 2) && (heads == 16 || heads == 32 || heads == 64 || heads == 128);
+    return (s_q == 1 || s_q == 2) && heads >= 16 && heads <= 128 && heads % 16 == 0;
 }
 
 // Work items the split kernel can take per row group: the plan makes at most one per resident
@@ -237,6 +249,8 @@ int launch_split(const FwdArgs& a, const LaunchGeom& g, hipStream_t s)
         hipLaunchKernelGGL(split_kernel<CfgR16>, dim3(a.capacity, g.row_groups), dim3(g.threads), g.lds_bytes, s, a);
         break;
     case kW32: hipLaunchKernelGGL(split_wide_kernel<CfgW32>, dim3(blocks), dim3(g.threads), g.lds_bytes, s, a); break;
+    case kSV1: hipLaunchKernelGGL(split_sv_kernel<CfgSV1>, dim3(blocks), dim3(g.threads), g.lds_bytes, s, a); break;
+    case kSV2: hipLaunchKernelGGL(split_sv_kernel<CfgSV2>, dim3(blocks), dim3(g.threads), g.lds_bytes, s, a); break;
     default: hipLaunchKernelGGL(split_wide_kernel<CfgW64>, dim3(blocks), dim3(g.threads), g.lds_bytes, s, a); break;
     }
     return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
@@ -590,7 +604,7 @@ const char* mla_decode_status_string(int status)
     switch (status) {
     case MLA_OK: return "MLA_OK";
     case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG: null pointer, bad size, alignment or non-finite scale";
-    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: heads must be 16/32/64/128, s_q 1 or 2, page size 64";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: heads must be a multiple of 16 in 16..128, s_q 1 or 2, page size 64";
     case MLA_ERR_WORKSPACE_TOO_SMALL: return "MLA_ERR_WORKSPACE_TOO_SMALL: see mla_decode_workspace_size";
     case MLA_ERR_NO_DEVICE: return "MLA_ERR_NO_DEVICE: no usable gfx950 HIP device";
     case MLA_ERR_HIP: return "MLA_ERR_HIP: a HIP runtime call failed";

@@ -95,7 +95,9 @@ def test_workspace_size_argument_errors(L):
     assert L.mla_decode_workspace_size(1, 1, 16, None) == -1
     assert L.mla_decode_workspace_size(0, 1, 16, ctypes.byref(n)) == -1
     assert L.mla_decode_workspace_size((1 << 20) + 1, 1, 16, ctypes.byref(n)) == -1
-    assert L.mla_decode_workspace_size(1, 2, 48, ctypes.byref(n)) == -2
+    # heads must be a multiple of 16 in 16..128: 48 is supported, 40 and 144 are not
+    assert L.mla_decode_workspace_size(1, 2, 40, ctypes.byref(n)) == -2
+    assert L.mla_decode_workspace_size(1, 1, 144, ctypes.byref(n)) == -2
 
 
 def _append(L, **kw):

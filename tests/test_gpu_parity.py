@@ -45,7 +45,9 @@ RAGGED = [1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 129, 1000, 4097]
 
 @pytest.mark.parametrize("heads,s_q,causal", [(16, 1, False), (16, 2, True), (16, 2, False), (32, 1, False),
                                              (32, 2, True), (64, 1, False), (64, 2, True), (128, 1, False),
-                                             (128, 2, True)])
+                                             (128, 2, True), (48, 1, False), (48, 2, True), (80, 1, False),
+                                             (80, 2, True), (96, 1, False), (96, 2, True), (112, 1, False),
+                                             (112, 2, True)])
 def test_ragged_lengths_all_row_configs(dev, heads, s_q, causal):
     lens = RAGGED if heads <= 32 else RAGGED[:10] + [700]
     case = make_case(f"ragged_h{heads}_sq{s_q}", batch=len(lens), s_q=s_q, heads=heads, seqlen=lens, seed=31,
