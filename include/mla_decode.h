@@ -135,6 +135,24 @@ int mla_decode_fwd_combine(const int32_t *seqlens, int bt_stride, int batch, int
                            float *lse, void *stream);
 
 /*
+ * For callers that cannot allocate device memory (code under stream capture, tight serving loops,
+ * harnesses that forbid allocation): mla_decode_plan followed by mla_decode_fwd in one call, with
+ * the workspace taken from a built-in device array of MLA_DECODE_NOALLOC_SCRATCH_BYTES per GPU
+ * (held from the library's load until the process ends).  No allocation is made by the call.
+ * Arguments mean what they mean for mla_decode_fwd; the results are bit-identical to
+ * mla_decode_plan + mla_decode_fwd on the same inputs.
+ *   Returns MLA_ERR_WORKSPACE_TOO_SMALL when the shape needs more than the built-in array
+ *   (mla_decode_workspace_size gives what a shape needs), and the other codes of mla_decode_fwd.
+ * Every call on a GPU uses that GPU's one array: calls that overlap in time on one GPU (other
+ * streams, other threads) race and give undefined results.  Calls ordered on one stream are safe.
+ */
+#define MLA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int mla_decode_fwd_noalloc(const void *q, const void *kv_cache, const int32_t *block_table,
+                           int bt_stride, const int32_t *seqlens, int batch, int s_q, int num_heads,
+                           int num_pages, int page_size, float softmax_scale, int causal, void *out,
+                           float *lse, void *stream);
+
+/*
  * GQA-path decode of GQLA: the latent expanded into g groups of keys and values, decoded as
  * standard grouped-query attention over a cache holding the group's keys and values plus the
  * shared RoPE key (GQLA summary, section "Arquitetura", item 2).  One GPU's share is one group:

@@ -13,6 +13,8 @@ Names follow the C ABI:
   * :func:`fwd`            -> ``mla_decode_fwd``
   * :func:`fwd_split`      -> ``mla_decode_fwd_split``   (first half of fwd)
   * :func:`fwd_combine`    -> ``mla_decode_fwd_combine`` (second half of fwd)
+  * :func:`fwd_noalloc`    -> ``mla_decode_fwd_noalloc`` (plan + fwd in the library's built-in
+    workspace, no allocation)
   * :func:`status_string`  -> ``mla_decode_status_string``
   * :func:`cache_append_rope` -> ``mla_cache_append_rope`` (new tokens into the paged cache)
   * :func:`gqa_workspace_size`, :func:`gqa_plan`, :func:`gqa_fwd` -> ``mla_gqa_decode_*`` (the
@@ -42,7 +44,7 @@ EXPORTS = ("mla_decode_workspace_size", "mla_decode_plan", "mla_decode_fwd", "ml
            "mla_decode_fwd_combine", "mla_decode_status_string", "mla_cache_append_rope",
            "mla_sparse_decode_workspace_size", "mla_sparse_decode_plan", "mla_sparse_decode_fwd",
            "mla_absorb_q", "mla_unabsorb_o", "mla_gqa_decode_workspace_size", "mla_gqa_decode_plan",
-           "mla_gqa_decode_fwd")
+           "mla_gqa_decode_fwd", "mla_decode_fwd_noalloc")
 GQA_D_H = 128
 GQA_ROW = 320
 D_NOPE = 128
@@ -74,6 +76,8 @@ def lib() -> ctypes.CDLL:
     L.mla_decode_fwd_split.restype = I
     L.mla_decode_fwd_combine.argtypes = [P, I, I, I, I, P, SZ, P, P, P]
     L.mla_decode_fwd_combine.restype = I
+    L.mla_decode_fwd_noalloc.argtypes = [P, P, P, I, P, I, I, I, I, I, ctypes.c_float, I, P, P, P]
+    L.mla_decode_fwd_noalloc.restype = I
     L.mla_cache_append_rope.argtypes = [P, P, P, P, P, I, P, I, I, I, I, I, ctypes.c_float, P]
     L.mla_cache_append_rope.restype = I
     L.mla_sparse_decode_workspace_size.argtypes = [I, I, I, I, ctypes.POINTER(SZ)]
@@ -201,6 +205,30 @@ def fwd_combine(seqlens, bt_stride: int, s_q: int, num_heads: int, workspace, ou
         raise ValueError("out must be [b, s_q, h, 512] and lse [b, s_q, h]")
     _check("mla_decode_fwd_combine", lib().mla_decode_fwd_combine(
         seqlens.data_ptr(), int(bt_stride), b, int(s_q), int(num_heads), workspace.data_ptr(), workspace.numel(),
+        out.data_ptr(), lse.data_ptr(), _stream(stream)))
+
+
+def fwd_noalloc(q, kv_cache, block_table, seqlens, softmax_scale: float, causal: bool, out, lse,
+                stream=None) -> None:
+    """mla_decode_fwd_noalloc: plan + fwd into ``out`` / ``lse`` using the library's built-in workspace."""
+    import torch
+    _require(q, "q", torch.bfloat16, 4)
+    dev = q.device
+    _require(kv_cache, "kv_cache", torch.bfloat16, 3, dev)
+    _require(block_table, "block_table", torch.int32, 2, dev)
+    _require(seqlens, "seqlens", torch.int32, 1, dev)
+    _require(out, "out", torch.bfloat16, 4, dev)
+    _require(lse, "lse", torch.float32, 3, dev)
+    b, s_q, h, dk = q.shape
+    if dk != D_K or kv_cache.shape[2] != D_K:
+        raise ValueError("q and kv_cache rows must be 576 wide")
+    if tuple(out.shape) != (b, s_q, h, D_V) or tuple(lse.shape) != (b, s_q, h):
+        raise ValueError("out must be [b, s_q, h, 512] and lse [b, s_q, h]")
+    if block_table.shape[0] != b or seqlens.shape[0] != b:
+        raise ValueError("block_table and seqlens need one row per sequence")
+    _check("mla_decode_fwd_noalloc", lib().mla_decode_fwd_noalloc(
+        q.data_ptr(), kv_cache.data_ptr(), block_table.data_ptr(), block_table.shape[1], seqlens.data_ptr(),
+        b, s_q, h, kv_cache.shape[0], kv_cache.shape[1], float(softmax_scale), int(bool(causal)),
         out.data_ptr(), lse.data_ptr(), _stream(stream)))
 
 

@@ -87,6 +87,38 @@ constexpr int kMaxDevices = 64;
 std::mutex g_mutex;
 DeviceInfo g_dev[kMaxDevices];
 
+// Built-in workspace of mla_decode_fwd_noalloc (every GPU the library runs on holds its own copy
+// until the process ends).  Host code never uses the array's name as an address: the device
+// address comes from hipGetSymbolAddress, once per device, with that device current.
+static __device__ __align__(256) char scratch[MLA_DECODE_NOALLOC_SCRATCH_BYTES];
+void* g_scratch_ptr[kMaxDevices];
+int g_scratch_status[kMaxDevices];
+bool g_scratch_ready[kMaxDevices];
+
+// the calling thread's current device's scratch address (nullptr on error)
+int scratch_address(void** out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return MLA_ERR_NO_DEVICE;
+    }
+    std::lock_guard<std::mutex> lock(g_mutex);
+    if (!g_scratch_ready[dev]) {
+        g_scratch_ready[dev] = true;
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+            (void)hipGetLastError();
+            g_scratch_status[dev] = MLA_ERR_HIP;
+        } else {
+            g_scratch_ptr[dev] = ptr;
+            g_scratch_status[dev] = MLA_OK;
+        }
+    }
+    *out = g_scratch_ptr[dev];
+    return g_scratch_status[dev];
+}
+
 int device_info(const DeviceInfo** out)
 {
     int count = 0;
@@ -303,6 +335,37 @@ int mla_decode_fwd_combine(const int32_t* seqlens, int bt_stride, int batch, int
                                &g);
     if (st != MLA_OK) return st;
     return launch_combine(a, static_cast<hipStream_t>(stream));
+}
+
+int mla_decode_fwd_noalloc(const void* q, const void* kv_cache, const int32_t* block_table, int bt_stride,
+                           const int32_t* seqlens, int batch, int s_q, int num_heads, int num_pages, int page_size,
+                           float softmax_scale, int causal, void* out, float* lse, void* stream)
+{
+    // argument checks and the size check against the built-in scratch, before its address is
+    // taken (the placeholder is never dereferenced)
+    FwdArgs a;
+    LaunchGeom g;
+    void* const placeholder = reinterpret_cast<void*>(uintptr_t(256));
+    int st = prepare_fwd(q, kv_cache, block_table, bt_stride, seqlens, batch, s_q, num_heads, num_pages, page_size,
+                         softmax_scale, causal, placeholder, MLA_DECODE_NOALLOC_SCRATCH_BYTES, out, lse, true, true,
+                         &a, &g);
+    if (st != MLA_OK) return st;
+    void* ws = nullptr;
+    st = scratch_address(&ws);
+    if (st != MLA_OK) return st;
+    a.ws = static_cast<char*>(ws);
+    const DeviceInfo* d = nullptr;
+    st = device_info(&d);
+    if (st != MLA_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // the plan writes every workspace field the split and combine kernels read: nothing needs
+    // clearing between calls
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, seqlens, batch, s_q, num_heads,
+                       s_q * num_heads, gx_of(*d, g), a.capacity, a.ws, -1);
+    if (hipGetLastError() != hipSuccess) return MLA_ERR_HIP;
+    st = launch_split(a, g, s);
+    if (st != MLA_OK) return st;
+    return launch_combine(a, s);
 }
 
 int mla_cache_append_rope(const void* kv_latent, const void* k_rope, void* q, void* kv_cache,
