@@ -87,6 +87,18 @@ int mla_decode_plan(const int32_t *seqlens, int batch, int s_q, int num_heads, v
                     size_t workspace_bytes, void *stream);
 
 /*
+ * mla_decode_plan with the work-item size chosen by the caller: every item holds at most
+ * chunk_pages pages (a sequence of p pages gets ceil(p / chunk_pages) items of balanced size),
+ * unless that many items would exceed the workspace's capacity, in which case the automatic size
+ * of mla_decode_plan is used.  chunk_pages = 0 is mla_decode_plan.  Any split gives the same
+ * attention up to fp32 rounding (the partial results are merged by LSE); it serves callers that
+ * fix their own split, and tests of that invariance.
+ *   chunk_pages  >= 0 (negative: MLA_ERR_INVALID_ARG); other arguments as for mla_decode_plan
+ */
+int mla_decode_plan_chunked(const int32_t *seqlens, int batch, int s_q, int num_heads, int chunk_pages,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Decode attention for one layer, using a plan made by mla_decode_plan with the
  * same seqlens, batch, s_q and num_heads.
  *   q            bf16 [batch][s_q][num_heads][576], contiguous

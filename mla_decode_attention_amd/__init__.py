@@ -9,7 +9,7 @@ PyTorch fallback -- if the library is missing, :func:`lib` raises.
 
 Names follow the C ABI:
   * :func:`workspace_size` -> ``mla_decode_workspace_size``
-  * :func:`plan`           -> ``mla_decode_plan``
+  * :func:`plan`           -> ``mla_decode_plan`` (``chunk_pages`` > 0: ``mla_decode_plan_chunked``)
   * :func:`fwd`            -> ``mla_decode_fwd``
   * :func:`fwd_split`      -> ``mla_decode_fwd_split``   (first half of fwd)
   * :func:`fwd_combine`    -> ``mla_decode_fwd_combine`` (second half of fwd)
@@ -44,7 +44,7 @@ EXPORTS = ("mla_decode_workspace_size", "mla_decode_plan", "mla_decode_fwd", "ml
            "mla_decode_fwd_combine", "mla_decode_status_string", "mla_cache_append_rope",
            "mla_sparse_decode_workspace_size", "mla_sparse_decode_plan", "mla_sparse_decode_fwd",
            "mla_absorb_q", "mla_unabsorb_o", "mla_gqa_decode_workspace_size", "mla_gqa_decode_plan",
-           "mla_gqa_decode_fwd", "mla_decode_fwd_noalloc")
+           "mla_gqa_decode_fwd", "mla_decode_fwd_noalloc", "mla_decode_plan_chunked")
 GQA_D_H = 128
 GQA_ROW = 320
 D_NOPE = 128
@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
     L.mla_decode_workspace_size.restype = I
     L.mla_decode_plan.argtypes = [P, I, I, I, P, SZ, P]
     L.mla_decode_plan.restype = I
+    L.mla_decode_plan_chunked.argtypes = [P, I, I, I, I, P, SZ, P]
+    L.mla_decode_plan_chunked.restype = I
     L.mla_decode_fwd.argtypes = [P, P, P, I, P, I, I, I, I, I, ctypes.c_float, I, P, SZ, P, P, P]
     L.mla_decode_fwd.restype = I
     L.mla_decode_fwd_split.argtypes = [P, P, P, I, P, I, I, I, I, I, ctypes.c_float, I, P, SZ, P]
@@ -141,11 +143,17 @@ def _require(t, name, dtype, ndim=None, device=None):
         raise ValueError(f"{name} must be contiguous")
 
 
-def plan(seqlens, s_q: int, num_heads: int, workspace, stream=None) -> None:
-    """mla_decode_plan: split metadata for these seqlens into ``workspace`` (uint8 device tensor)."""
+def plan(seqlens, s_q: int, num_heads: int, workspace, stream=None, chunk_pages: int = 0) -> None:
+    """mla_decode_plan: split metadata for these seqlens into ``workspace`` (uint8 device tensor);
+    ``chunk_pages`` > 0 caps the pages per work item (mla_decode_plan_chunked)."""
     import torch
     _require(seqlens, "seqlens", torch.int32, 1)
     _require(workspace, "workspace", torch.uint8, 1, seqlens.device)
+    if chunk_pages:
+        _check("mla_decode_plan_chunked", lib().mla_decode_plan_chunked(
+            seqlens.data_ptr(), seqlens.shape[0], int(s_q), int(num_heads), int(chunk_pages), workspace.data_ptr(),
+            workspace.numel(), _stream(stream)))
+        return
     _check("mla_decode_plan", lib().mla_decode_plan(seqlens.data_ptr(), seqlens.shape[0], int(s_q), int(num_heads),
                                                     workspace.data_ptr(), workspace.numel(), _stream(stream)))
 

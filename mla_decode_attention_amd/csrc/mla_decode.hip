@@ -208,10 +208,10 @@ int mla_decode_workspace_size(int batch, int s_q, int num_heads, size_t* bytes)
     return MLA_OK;
 }
 
-int mla_decode_plan(const int32_t* seqlens, int batch, int s_q, int num_heads, void* workspace,
-                    size_t workspace_bytes, void* stream)
+int mla_decode_plan_chunked(const int32_t* seqlens, int batch, int s_q, int num_heads, int chunk_pages,
+                            void* workspace, size_t workspace_bytes, void* stream)
 {
-    if (!seqlens || !workspace || !batch_ok(batch)) return MLA_ERR_INVALID_ARG;
+    if (!seqlens || !workspace || !batch_ok(batch) || chunk_pages < 0) return MLA_ERR_INVALID_ARG;
     if (!aligned(workspace, 256) || !aligned(seqlens, 4)) return MLA_ERR_INVALID_ARG;
     if (!heads_ok(s_q, num_heads)) return MLA_ERR_UNSUPPORTED;
     const DeviceInfo* d = nullptr;
@@ -222,8 +222,15 @@ int mla_decode_plan(const int32_t* seqlens, int batch, int s_q, int num_heads, v
     const int cap = item_capacity(*d, g, batch);
     if (workspace_bytes < ws_layout(batch, s_q * num_heads, cap).total) return MLA_ERR_WORKSPACE_TOO_SMALL;
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, static_cast<hipStream_t>(stream), seqlens,
-                       batch, s_q, num_heads, s_q * num_heads, gx_of(*d, g), cap, static_cast<char*>(workspace), -1);
+                       batch, s_q, num_heads, s_q * num_heads, gx_of(*d, g), cap, static_cast<char*>(workspace), -1,
+                       chunk_pages);
     return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int mla_decode_plan(const int32_t* seqlens, int batch, int s_q, int num_heads, void* workspace,
+                    size_t workspace_bytes, void* stream)
+{
+    return mla_decode_plan_chunked(seqlens, batch, s_q, num_heads, 0, workspace, workspace_bytes, stream);
 }
 
 namespace {

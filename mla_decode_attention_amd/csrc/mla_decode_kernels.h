@@ -94,10 +94,12 @@ constexpr long long kWeightMinPages = 8192; // plans this large stream from HBM 
 __device__ inline int pages_of(int L) { return L <= 0 ? 0 : L / kPage + (L % kPage != 0 ? 1 : 0); }
 
 // uniform_len >= 0: every sequence has that length and `seqlens` is not read (sparse decode: each
-// query token is a sequence of top-k index slots)
+// query token is a sequence of top-k index slots).  force_chunk > 0: items of at most that many
+// pages, unless their count would exceed the workspace's capacity (then the automatic chunk)
 __global__ void __launch_bounds__(kPlanThreads) plan_kernel(const int32_t* __restrict__ seqlens, int batch,
                                                             int s_q, int heads, int rows, int gx,
-                                                            int capacity, char* __restrict__ ws, int uniform_len)
+                                                            int capacity, char* __restrict__ ws, int uniform_len,
+                                                            int force_chunk = 0)
 {
     auto len_of = [&](int b) { return uniform_len >= 0 ? uniform_len : seqlens[b]; };
     const WsLayout lay = ws_layout(batch, rows, capacity);
@@ -161,6 +163,8 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(const int32_t* __res
         chunk = mx;
     }
     if (chunk < 1) chunk = 1;
+    // a caller-chosen chunk replaces the automatic one when its items fit the workspace
+    if (force_chunk > 0 && items_for(force_chunk) <= capacity) chunk = force_chunk;
 
     // per-sequence split counts, exclusive prefix sum in blocks of kPlanThreads
     for (int base = 0; base < batch; base += kPlanThreads) {

@@ -58,6 +58,9 @@ def _load(planted_mistake: int = 0) -> ctypes.CDLL:
     lib.oracle_mla_decode.argtypes = [_P, _P, _P, _I64, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
                                       ctypes.c_double, ctypes.c_int, _P, _I64, _P, _P, ctypes.c_int]
     lib.oracle_mla_decode.restype = ctypes.c_int
+    lib.oracle_mla_decode_with_scale.argtypes = [_P, _P, _P, _I64, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I64,
+                                                 ctypes.c_double, ctypes.c_int, _P, _I64, _P, _P, _P, ctypes.c_int]
+    lib.oracle_mla_decode_with_scale.restype = ctypes.c_int
     _LIBS[planted_mistake] = lib
     return lib
 
@@ -90,8 +93,10 @@ class Oracle:
         return (o, lse, p) if return_probs else (o, lse)
 
     def mla_decode(self, q_bits, cache_bits, block_table, seqlens, scale: float, causal: bool,
-                   d_v: int = 512, rows=None, threads: int | None = None):
-        """fp64 O and LSE for the given rows (default: all, shaped [b, s_q, h, d_v] and [b, s_q, h])."""
+                   d_v: int = 512, rows=None, threads: int | None = None, with_scale: bool = False):
+        """fp64 O and LSE for the given rows (default: all, shaped [b, s_q, h, d_v] and [b, s_q, h]).
+        with_scale: also sum_j p_j |v_j| per element (shaped like O), the error scale of rounding the
+        weights before the weighted sum."""
         q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
         cache_bits = np.ascontiguousarray(cache_bits, dtype=np.uint16)
         block_table = np.ascontiguousarray(block_table, dtype=np.int32)
@@ -104,14 +109,23 @@ class Oracle:
         o = np.empty((n_rows, d_v))
         lse = np.empty(n_rows)
         threads = threads or (os.cpu_count() or 1)
-        rc = self.lib.oracle_mla_decode(_ptr(q_bits), _ptr(cache_bits), _ptr(block_table), block_table.shape[1],
-                                        _ptr(seqlens), b, s_q, h, num_pages, page_size, d_k, d_v, float(scale),
-                                        int(bool(causal)), _ptr(sel), n_rows, _ptr(o), _ptr(lse), int(threads))
+        if with_scale:
+            o_abs = np.empty((n_rows, d_v))
+            rc = self.lib.oracle_mla_decode_with_scale(
+                _ptr(q_bits), _ptr(cache_bits), _ptr(block_table), block_table.shape[1], _ptr(seqlens), b, s_q, h,
+                num_pages, page_size, d_k, d_v, float(scale), int(bool(causal)), _ptr(sel), n_rows, _ptr(o),
+                _ptr(o_abs), _ptr(lse), int(threads))
+        else:
+            o_abs = None
+            rc = self.lib.oracle_mla_decode(_ptr(q_bits), _ptr(cache_bits), _ptr(block_table), block_table.shape[1],
+                                            _ptr(seqlens), b, s_q, h, num_pages, page_size, d_k, d_v, float(scale),
+                                            int(bool(causal)), _ptr(sel), n_rows, _ptr(o), _ptr(lse), int(threads))
         if rc != 0:
             raise RuntimeError(f"oracle_mla_decode failed: {rc}")
         if sel is None:
-            return o.reshape(b, s_q, h, d_v), lse.reshape(b, s_q, h)
-        return o, lse
+            o, lse = o.reshape(b, s_q, h, d_v), lse.reshape(b, s_q, h)
+            o_abs = None if o_abs is None else o_abs.reshape(b, s_q, h, d_v)
+        return (o, lse, o_abs) if with_scale else (o, lse)
 
 
 _DEFAULT: Oracle | None = None
@@ -128,8 +142,10 @@ def attention(q, k, v, scale: float, return_probs: bool = False):
     return default().attention(q, k, v, scale, return_probs)
 
 
-def mla_decode(q_bits, cache_bits, block_table, seqlens, scale, causal, d_v=512, rows=None, threads=None):
-    return default().mla_decode(q_bits, cache_bits, block_table, seqlens, scale, causal, d_v, rows, threads)
+def mla_decode(q_bits, cache_bits, block_table, seqlens, scale, causal, d_v=512, rows=None, threads=None,
+               with_scale=False):
+    return default().mla_decode(q_bits, cache_bits, block_table, seqlens, scale, causal, d_v, rows, threads,
+                                with_scale)
 
 
 def _bf16_f64(bits) -> np.ndarray:

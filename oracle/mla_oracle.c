@@ -145,11 +145,46 @@ int oracle_attention_f64(int64_t n_q, int64_t n_k, int64_t d_k, int64_t d_v,
  *   o, lse      fp64 [n_rows][d_v], [n_rows]
  * Returns ORACLE_ERR_PAGE if a page a visible key needs is outside the pool.
  */
+static int decode_rows(const uint16_t *q, const uint16_t *cache, const int32_t *block_table,
+                       int64_t bt_stride, const int32_t *seqlens, int64_t batch, int64_t s_q,
+                       int64_t heads, int64_t num_pages, int64_t page_size, int64_t d_k,
+                       int64_t d_v, double scale, int causal, const int64_t *rows,
+                       int64_t n_rows, double *o, double *o_abs, double *lse, int n_threads);
+
 int oracle_mla_decode(const uint16_t *q, const uint16_t *cache, const int32_t *block_table,
                       int64_t bt_stride, const int32_t *seqlens, int64_t batch, int64_t s_q,
                       int64_t heads, int64_t num_pages, int64_t page_size, int64_t d_k,
                       int64_t d_v, double scale, int causal, const int64_t *rows,
                       int64_t n_rows, double *o, double *lse, int n_threads)
+{
+    return decode_rows(q, cache, block_table, bt_stride, seqlens, batch, s_q, heads, num_pages,
+                       page_size, d_k, d_v, scale, causal, rows, n_rows, o, NULL, lse, n_threads);
+}
+
+/*
+ * The same, with a second output o_abs[n_rows][d_v] = sum_j p_j |v_j| (the attention of the
+ * absolute values under the same weights).  It is the scale of the error that rounding the
+ * weights p_j (to a short format, before the weighted sum) can cause in O, so the tests derive
+ * their per-element tolerance from it; it bounds |O| elementwise and equals it when every value
+ * is nonnegative.
+ */
+int oracle_mla_decode_with_scale(const uint16_t *q, const uint16_t *cache, const int32_t *block_table,
+                                 int64_t bt_stride, const int32_t *seqlens, int64_t batch, int64_t s_q,
+                                 int64_t heads, int64_t num_pages, int64_t page_size, int64_t d_k,
+                                 int64_t d_v, double scale, int causal, const int64_t *rows,
+                                 int64_t n_rows, double *o, double *o_abs, double *lse, int n_threads)
+{
+    if (!o_abs)
+        return ORACLE_ERR_ARG;
+    return decode_rows(q, cache, block_table, bt_stride, seqlens, batch, s_q, heads, num_pages,
+                       page_size, d_k, d_v, scale, causal, rows, n_rows, o, o_abs, lse, n_threads);
+}
+
+static int decode_rows(const uint16_t *q, const uint16_t *cache, const int32_t *block_table,
+                       int64_t bt_stride, const int32_t *seqlens, int64_t batch, int64_t s_q,
+                       int64_t heads, int64_t num_pages, int64_t page_size, int64_t d_k,
+                       int64_t d_v, double scale, int causal, const int64_t *rows,
+                       int64_t n_rows, double *o, double *o_abs, double *lse, int n_threads)
 {
     if (!q || !cache || !block_table || !seqlens || !o || !lse || batch <= 0 || s_q <= 0 ||
         heads <= 0 || num_pages <= 0 || page_size <= 0 || d_k <= 0 || d_v <= 0 || d_v > d_k ||
@@ -183,8 +218,12 @@ int oracle_mla_decode(const uint16_t *q, const uint16_t *cache, const int32_t *b
         if (n > L)
             n = L;
         double *orow = o + t * d_v;
+        double *arow = o_abs ? o_abs + t * d_v : NULL;
         for (int64_t d = 0; d < d_v; ++d)
             orow[d] = 0.0;
+        if (arow)
+            for (int64_t d = 0; d < d_v; ++d)
+                arow[d] = 0.0;
         if (n == 0) {
             lse[t] = -INFINITY;
             continue;
@@ -240,9 +279,15 @@ int oracle_mla_decode(const uint16_t *q, const uint16_t *cache, const int32_t *b
 #endif
             for (int64_t d = 0; d < d_v; ++d)
                 orow[d] += w[j] * bf16_to_f64(vrow[d]);
+            if (arow)
+                for (int64_t d = 0; d < d_v; ++d)
+                    arow[d] += w[j] * fabs(bf16_to_f64(vrow[d]));
         }
         for (int64_t d = 0; d < d_v; ++d)
             orow[d] /= l;
+        if (arow)
+            for (int64_t d = 0; d < d_v; ++d)
+                arow[d] /= l;
         lse[t] = finish_lse(m, l);
         free(w);
         free((void *)keys);

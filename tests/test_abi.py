@@ -90,6 +90,16 @@ def test_plan_argument_errors(L):
     assert L.mla_decode_plan(P(FAKE), 1, 1, 20, ws, 1 << 20, None) == -2
 
 
+def test_plan_chunked_argument_errors(L):
+    ws = P(FAKE)
+    assert L.mla_decode_plan_chunked(P(FAKE), 1, 1, 16, -1, ws, 1 << 20, None) == -1   # negative chunk
+    assert L.mla_decode_plan_chunked(None, 1, 1, 16, 4, ws, 1 << 20, None) == -1
+    assert L.mla_decode_plan_chunked(P(FAKE), 0, 1, 16, 4, ws, 1 << 20, None) == -1
+    assert L.mla_decode_plan_chunked(P(FAKE), 1, 1, 16, 4, P(FAKE + 4), 1 << 20, None) == -1
+    assert L.mla_decode_plan_chunked(P(FAKE), 1, 3, 16, 4, ws, 1 << 20, None) == -2
+    assert L.mla_decode_plan_chunked(P(FAKE), 1, 1, 20, 4, ws, 1 << 20, None) == -2
+
+
 def test_workspace_size_argument_errors(L):
     n = ctypes.c_size_t(0)
     assert L.mla_decode_workspace_size(1, 1, 16, None) == -1

@@ -18,26 +18,14 @@ def full_parity(case, dev, what=None):
     log(f"case {what}: b={case.batch} s_q={case.s_q} h={case.heads} L={case.seqlens.tolist()[:6]} "
         f"causal={case.causal} pages={case.num_pages}")
     o, l = run_gpu(case, dev)
-    ro, rl = oracle.mla_decode(case.q, case.cache, case.block_table, case.seqlens, case.softmax_scale, case.causal)
-    return parity(o, l, ro, rl, what)
+    ro, rl, rs = oracle.mla_decode(case.q, case.cache, case.block_table, case.seqlens, case.softmax_scale,
+                                   case.causal, with_scale=True)
+    return parity(o, l, ro, rl, what, scale=rs)
 
 
 @pytest.mark.parametrize("name", ["tiny_b1_h16_L256", "paged_b16_h16_L4096", "mtp_b16_h16_sq2_L8K-16K"])
 def test_workload_full(dev, name):
     full_parity(workloads.build(name), dev)
-
-
-@pytest.mark.parametrize("name,n_rows", [("long_b16_h16_L65536", 48), ("allheads_b8_h128_L32768", 64)])
-def test_workload_sampled_rows(dev, name, n_rows):
-    """Full-size workloads in the benchmark's launch configuration; the oracle computes sampled rows."""
-    case = workloads.build(name)
-    log(f"case {name}: generated, running on GPU")
-    o, l = run_gpu(case, dev)
-    rng = np.random.default_rng(99)
-    rows = np.sort(rng.choice(case.rows, n_rows, replace=False))
-    ro, rl = oracle.mla_decode(case.q, case.cache, case.block_table, case.seqlens, case.softmax_scale,
-                               case.causal, rows=rows)
-    parity(o.reshape(case.rows, -1)[rows], l.reshape(-1)[rows], ro, rl, f"{name} ({n_rows} sampled rows)")
 
 
 RAGGED = [1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 129, 1000, 4097]
