@@ -83,7 +83,7 @@ def source_code_digest(texts) -> str:
 
 def kernel_source_digest() -> str:
     texts = []
-    for f in ("mla_decode_kernels.h", "mla_decode.hip"):
+    for f in ("mla_decode_kernels.h", "mla_sv_kernel.h", "mla_decode.hip"):
         with open(os.path.join(ROOT, "mla_decode_attention_amd", "csrc", f)) as fh:
             texts.append(fh.read())
     return source_code_digest(texts)
@@ -179,6 +179,79 @@ def _cpu_model() -> str:
     except OSError:
         pass
     return "unknown"
+
+
+def measure_workload(mla, name: str, dev, steps: int, warmup: int, parity_rows: int):
+    """One of the other configured workloads, timed like the headline: step (split + combine) and
+    split-kernel durations, algorithmic TB/s and MFMA utilisation, and raw parity of the first
+    parity_rows query rows against the fp64 oracle (reported, not asserted)."""
+    import numpy as np
+    import torch
+
+    from mla_decode_attention_amd import workloads as W
+    from mla_decode_attention_amd.inputs import bf16_bits_to_f32
+    stream = torch.cuda.current_stream()
+    case = W.build(name)
+    q = torch.from_numpy(case.q.view(np.int16)).to(dev).view(torch.bfloat16)
+    cache = torch.from_numpy(case.cache.view(np.int16)).to(dev).view(torch.bfloat16)
+    bt = torch.from_numpy(case.block_table).to(dev)
+    sl = torch.from_numpy(case.seqlens).to(dev)
+    b, s_q, h = case.batch, case.s_q, case.heads
+    ws = torch.empty(mla.workspace_size(b, s_q, h), dtype=torch.uint8, device=dev)
+    out = torch.empty((b, s_q, h, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((b, s_q, h), dtype=torch.float32, device=dev)
+    mla.plan(sl, s_q, h, ws)
+    split_c = c_calls(mla, lambda: mla.fwd_split(q, cache, bt, sl, case.softmax_scale, case.causal, ws))
+    combine_c = c_calls(mla, lambda: mla.fwd_combine(sl, bt.shape[1], s_q, h, ws, out, lse))
+    for _ in range(warmup):
+        split_c()
+        combine_c()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        split_c()
+        combine_c()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    step_us = e0.elapsed_time(e1) * 1e3 / steps
+    ea = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    eb = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for k in range(steps):
+        ea[k].record(stream)
+        split_c()
+        eb[k].record(stream)
+        combine_c()
+    torch.cuda.synchronize()
+    split_us = float(np.mean([ea[k].elapsed_time(eb[k]) for k in range(steps)])) * 1e3
+    nbytes = W.algorithmic_bytes(case.seqlens, b, s_q, h)
+    flops = W.algorithmic_flops(case.seqlens, s_q, h, case.causal)
+    kv_q = int(case.seqlens.astype(np.int64).sum()) * W.ROW_BYTES + b * s_q * h * 576 * 2
+    rec = {"us_per_step": round(step_us, 2), "split_avg_us": round(split_us, 2),
+           "TB/s": round(nbytes / step_us / 1e6, 4), "pct_of_hbm_peak": round(100 * nbytes / step_us / 1e3 / HBM_PEAK_GBS, 2),
+           "split_GB/s": round(kv_q / split_us / 1e3, 1),
+           "mfma_util_step": round(flops / step_us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
+           "mfma_util_split": round(flops / split_us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
+           "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+           "config": {"batch": b, "s_q": s_q, "heads": h, "causal": bool(case.causal),
+                      "context": [int(case.seqlens.min()), int(case.seqlens.max())]}}
+    try:
+        import oracle
+        rows = np.arange(min(parity_rows, case.rows), dtype=np.int64)
+        og = bf16_bits_to_f32(out.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+        lg = lse.cpu().numpy().astype(np.float64).reshape(-1)[rows]
+        ro, rl = oracle.mla_decode(case.q, case.cache, case.block_table, case.seqlens, case.softmax_scale,
+                                   case.causal, rows=rows)
+        err = np.abs(og.reshape(case.rows, -1)[rows] - ro)
+        rec["parity_sampled_rows"] = {
+            "rows": int(rows.size), "o_maxabs": float(err.max()), "o_rmse": float(np.sqrt(np.mean(err ** 2))),
+            "o_maxabs_over_max1_maxO": float(err.max() / max(1.0, np.abs(ro).max())),
+            "lse_rel": float(np.max(np.abs(lg - rl) / np.maximum(1.0, np.abs(rl))))}
+    except Exception as exc:   # the timing stands without the check
+        rec["parity_sampled_rows"] = f"skipped: {exc}"
+    del q, cache, ws
+    torch.cuda.empty_cache()
+    return rec
 
 
 def measure_extras(mla, case, dev, q, cache, bt, sl, steps: int):
@@ -452,7 +525,7 @@ def main() -> int:
     split_gbs = kv_q_bytes / (split_avg_ms * 1e-3) / 1e9
     mfma_util = step_flops / (ms_per_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS
     split_flops = step_flops   # every FLOP of the step is in the split kernel
-    split_name = "split_wide_kernel" if s_q * h >= 32 else "split_kernel"
+    split_name = "split_kernel" if s_q * h <= 16 else "split_sv_kernel"
     if flushed is not None:
         flushed["TB/s"] = round(step_bytes / (flushed["median_us_per_step"] * 1e-6) / 1e12, 4)
         flushed["split_GB/s"] = round(kv_q_bytes / (flushed["median_split_us"] * 1e-6) / 1e9, 1)
@@ -478,6 +551,19 @@ def main() -> int:
         except Exception as exc:   # the headline line stands without them
             extras = {"error": f"{type(exc).__name__}: {exc}"}
         log(f"extras: {extras}")
+        # the other configured workloads, timed the same way
+        wl = {}
+        for other, prow in (("paged_b16_h16_L4096", 16), ("mtp_b16_h16_sq2_L8K-16K", 32),
+                            ("allheads_b8_h128_L32768", 128)):
+            if other == name:
+                continue
+            log(f"extras: workload {other}")
+            try:
+                wl[other] = measure_workload(mla, other, dev, K, args.warmup, prow)
+            except Exception as exc:
+                wl[other] = {"error": f"{type(exc).__name__}: {exc}"}
+            log(f"extras: {other}: {wl[other]}")
+        extras["workloads"] = wl
 
     cpu, parity = None, None
     if not args.no_cpu_baseline:
