@@ -158,7 +158,9 @@ int mla_decode_fwd_combine(const int32_t *seqlens, int bt_stride, int batch, int
  * Every call on a GPU uses that GPU's one array: calls that overlap in time on one GPU (other
  * streams, other threads) race and give undefined results.  Calls ordered on one stream are safe.
  */
-#define MLA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+/* 128 MiB: on a 256-CU MI355X up to 382 sequences of 128 heads (191 with two query tokens), or
+ * 3,829 sequences of 16 heads */
+#define MLA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
 int mla_decode_fwd_noalloc(const void *q, const void *kv_cache, const int32_t *block_table,
                            int bt_stride, const int32_t *seqlens, int batch, int s_q, int num_heads,
                            int num_pages, int page_size, float softmax_scale, int causal, void *out,

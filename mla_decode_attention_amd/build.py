@@ -21,12 +21,12 @@ FLAGS = [
     "-Wall", "-Wno-unused-function",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
+# translation units of the library and whether each keeps the arch-VGPR accumulator option; the
+# 128-row kernel holds 256 accumulators per lane, which only fit in the AGPRs
+UNITS = [("mla_decode.hip", True), ("mla_rw.hip", False)]
 
 
-def build(verbose: bool = False, extra_flags: list[str] | None = None, out: str | None = None) -> str:
-    out = out or LIB
-    tmp = f"{out}.tmp{os.getpid()}"
-    cmd = [HIPCC, *FLAGS, *(extra_flags or []), os.path.join(CSRC, "mla_decode.hip"), "-o", tmp]
+def _run(cmd: list[str], verbose: bool) -> None:
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -35,6 +35,31 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None, out: str 
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msgs}")
     if verbose and msgs.strip():
         print(msgs)
+
+
+def build(verbose: bool = False, extra_flags: list[str] | None = None, out: str | None = None,
+          csrc: str | None = None) -> str:
+    """Compile every translation unit to an object, then link the shared library.  extra_flags go
+    to every compile; csrc replaces the source folder (for builds of modified copies)."""
+    out = out or LIB
+    src = csrc or CSRC
+    tag = f"{os.getpid()}"
+    objs = []
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+    compile_flags = [src if f == CSRC else f for f in compile_flags]
+    try:
+        for name, vgpr_form in UNITS:
+            obj = f"{out}.{name}.{tag}.o"
+            fl = compile_flags if vgpr_form else [f for f in compile_flags
+                                                  if f not in ("-mllvm", "-amdgpu-mfma-vgpr-form=1")]
+            _run([HIPCC, *fl, *(extra_flags or []), "-c", os.path.join(src, name), "-o", obj], verbose)
+            objs.append(obj)
+        tmp = f"{out}.tmp{tag}"
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
     os.replace(tmp, out)
     return out
 

@@ -37,6 +37,15 @@
 
 #include "mla_decode_kernels.h"
 
+// LDS-read look-ahead of the score waves (K operands, in k-steps) and of the value waves (V^T
+// operand pairs)
+#ifndef MLA_SV_KD
+#define MLA_SV_KD 3
+#endif
+#ifndef MLA_SV_VD
+#define MLA_SV_VD 2
+#endif
+
 namespace mla {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -70,19 +79,6 @@ struct SvCfg {
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
     static_assert(RW * kOutRow <= NS * LDS_TILE, "partial rows fit the tile stages");
 };
-
-// LDS-destination buffer load of 16 B per lane: lane l's bytes land at LDS byte lds + 16 l (M0
-// holds the wave's LDS address).  Written as inline asm, with no register output, so that the
-// compiler, which cannot tell the tile being loaded from the tiles being read, does not make the
-// wave's LDS reads wait for it; the issuing wave waits for its own loads (vm_wait_all) before the
-// barrier that publishes the tile.
-__device__ inline void lds_load_16(__amdgpu_buffer_rsrc_t r, uint32_t lds, int voffset)
-{
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voffset), "s"(r)
-                 : "memory", "m0");
-}
-
-__device__ inline void vm_wait_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0) only
 
 template <class C>
 __global__ void __launch_bounds__(C::THREADS) split_sv_kernel(FwdArgs a)
@@ -154,7 +150,7 @@ __global__ void __launch_bounds__(C::THREADS) split_sv_kernel(FwdArgs a)
         }
         // K operand of k-step j: token 16 th + lr of the tile, dims 32 j + 8 lg .. + 8
         const int kbase = (16 * th + lr) * C::LROW + 16 * lg;
-        constexpr int KD = 3;   // K-operand look-ahead (k-steps)
+        constexpr int KD = MLA_SV_KD;   // K-operand look-ahead (k-steps)
         // The 16x16 result: lane (lr, lg), register i holds S^T[token 16 th + 4 lg + i][row 16 h + lr].
         // Those four tokens are the value product's B-operand elements 4 (lg >> 1) .. + 3 of lane
         // 16 h + lr + 32 (lg & 1), k-step th.
@@ -352,7 +348,7 @@ __global__ void __launch_bounds__(C::THREADS) split_sv_kernel(FwdArgs a)
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) pop[rb][ks] = *reinterpret_cast<const bf16x8*>(pb + rb * 2048 + ks * 1024);
             const char* vt = stage(tv) + vbase;
-            constexpr int VD = 2;   // look-ahead in operands (ks, d pairs)
+            constexpr int VD = MLA_SV_VD;   // look-ahead in operands (ks, d pairs)
             i16x4 vlo[VD + 1], vhi[VD + 1];
 #pragma unroll
             for (int i = 0; i < VD; ++i) {
