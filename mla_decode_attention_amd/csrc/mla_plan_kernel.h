@@ -21,6 +21,7 @@ constexpr int kPlanThreads = 1024;
 constexpr long long kEvenXcdWeight = 16;   // relative work of an item on an even XCD
 constexpr long long kOddXcdWeight = 15;    // ... and on an odd one (see the plan kernel)
 constexpr long long kWeightMinPages = 8192; // plans this large stream from HBM (>= 604 MB of rows)
+constexpr int kPlanCache = 4;               // sequences per thread whose page counts stay in registers
 
 // no L + 63 (which overflows int for L within 63 of INT_MAX)
 __device__ inline int pages_of(int L) { return L <= 0 ? 0 : L / kPage + (L % kPage != 0 ? 1 : 0); }
@@ -45,13 +46,35 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(const int32_t* __res
     __shared__ int wave_tot[kPlanThreads / 64];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
 
-    // total pages
+    // page counts, read once: the first kPlanCache * kPlanThreads sequences' counts stay in
+    // registers for the passes below (each pass would otherwise wait on a memory round trip)
+    int pg_c[kPlanCache];
     long long mine = 0;
-    for (int b = tid; b < batch; b += kPlanThreads) {
+#pragma unroll
+    for (int i = 0; i < kPlanCache; ++i) {
+        const int b = tid + i * kPlanThreads;
+        int p = 0;
+        if (b < batch) {
+            const int L = len_of(b);
+            ws_len[b] = L;
+            p = pages_of(L);
+        }
+        pg_c[i] = p;
+        mine += p;
+    }
+    for (int b = tid + kPlanCache * kPlanThreads; b < batch; b += kPlanThreads) {
         const int L = len_of(b);
         ws_len[b] = L;
         mine += pages_of(L);
     }
+    // f(pages) summed over this thread's sequences
+    auto sum_pages = [&](auto f) {
+        long long n = 0;
+#pragma unroll
+        for (int i = 0; i < kPlanCache; ++i) n += f(pg_c[i]);   // 0 pages for b >= batch: f(0) == 0 below
+        for (int b = tid + kPlanCache * kPlanThreads; b < batch; b += kPlanThreads) n += f(pages_of(len_of(b)));
+        return n;
+    };
     // block-wide sum (every thread gets it); two barriers so that red[] can be reused
     auto block_sum = [&](long long v) {
         for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
@@ -64,11 +87,7 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(const int32_t* __res
     };
     if (tid == 0) scan_carry = 0;
     const long long total = block_sum(mine);
-    auto items_for = [&](long long c) {
-        long long n = 0;
-        for (int b = tid; b < batch; b += kPlanThreads) n += (pages_of(len_of(b)) + c - 1) / c;
-        return block_sum(n);
-    };
+    auto items_for = [&](long long c) { return block_sum(sum_pages([&](int pg) { return (pg + c - 1) / c; })); };
     const long long slots = gx > 0 ? gx : 1;
     long long chunk;
     if (slots > batch) {
@@ -86,7 +105,10 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(const int32_t* __res
         chunk = lo;
     } else {
         long long mx = 0;
-        for (int b = tid; b < batch; b += kPlanThreads) mx = max(mx, (long long)pages_of(len_of(b)));
+#pragma unroll
+        for (int i = 0; i < kPlanCache; ++i) mx = max(mx, (long long)pg_c[i]);
+        for (int b = tid + kPlanCache * kPlanThreads; b < batch; b += kPlanThreads)
+            mx = max(mx, (long long)pages_of(len_of(b)));
         for (int o = 32; o > 0; o >>= 1) mx = max(mx, __shfl_xor(mx, o));
         __syncthreads();
         if (lane == 0) red[wid] = mx;
@@ -99,13 +121,9 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(const int32_t* __res
     if (force_chunk > 0 && items_for(force_chunk) <= capacity) chunk = force_chunk;
 
     // per-sequence split counts, exclusive prefix sum in blocks of kPlanThreads
-    for (int base = 0; base < batch; base += kPlanThreads) {
+    auto block_items = [&](int base, int pg) __attribute__((always_inline)) {
         const int b = base + tid;
-        int n = 0, pg = 0;
-        if (b < batch) {
-            pg = pages_of(len_of(b));
-            n = int((pg + chunk - 1) / chunk);
-        }
+        const int n = b < batch ? int((pg + chunk - 1) / chunk) : 0;
         int incl = n;
         for (int o = 1; o < 64; o <<= 1) {
             const int t = __shfl_up(incl, o);
@@ -141,7 +159,12 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(const int32_t* __res
         __syncthreads();
         if (tid == kPlanThreads - 1) scan_carry = excl + n;
         __syncthreads();
-    }
+    };
+#pragma unroll
+    for (int i = 0; i < kPlanCache; ++i)
+        if (i * kPlanThreads < batch) block_items(i * kPlanThreads, pg_c[i]);   // uniform branch
+    for (int base = kPlanCache * kPlanThreads; base < batch; base += kPlanThreads)
+        block_items(base, base + tid < batch ? pages_of(len_of(base + tid)) : 0);
     if (tid == 0) {
         bsplit[batch] = scan_carry;
         header[kHMagic] = kPlanMagic;

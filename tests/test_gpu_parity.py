@@ -180,11 +180,14 @@ def _plan_lens(kind):
         "near_int_max": lambda: [2 ** 31 - 1, 2 ** 31 - 64, 5, 0],
         # the headline's lengths: a plan large enough for the XCD weighting of the items
         "headline_like": lambda: [65536] * 16,
+        # more sequences than the plan kernel keeps in registers (4 per thread of 1024)
+        "beyond_register_cache": lambda: [int(x) for x in rng.integers(0, 300, 5000)],
     }[kind]()
 
 
 @pytest.mark.parametrize("lens_kind", ["mixed", "batch_beyond_slots", "all_empty", "one_huge", "many_tiny",
-                                       "uneven_like_mtp", "batch_near_slots", "near_int_max", "headline_like"])
+                                       "uneven_like_mtp", "batch_near_slots", "near_int_max", "headline_like",
+                                       "beyond_register_cache"])
 def test_plan_covers_every_page_once(dev, lens_kind):
     """Read the plan back: items tile each sequence's pages exactly once, in balanced chunks of the
     smallest size that fits one wave of split workgroups (one item per sequence once the batch
