@@ -27,7 +27,6 @@ namespace mla {
 const void* split_rw_fn();
 int split_rw_threads();
 int split_rw_lds_bytes();
-int split_rw_rows();
 void launch_split_rw(const FwdArgs& a, int blocks, hipStream_t s);
 }  // namespace mla
 
@@ -41,10 +40,6 @@ using namespace mla;
 // eight-wave score/value form, whose two waves per SIMD overlap MFMA, LDS and vector work.
 //                         waves  row-blocks  segments  tile tokens  LDS stages  register tiles
 using CfgR16 = SplitCfg<4, 1, 1, 16, 1, 1>;    // 4 independent waves, one 18 KiB tile each
-//                     register tiles  score-wave load units  16-row blocks
-using CfgW32 = WideCfg<1, 5, 2>;               // 32 rows per workgroup
-using CfgW64 = WideCfg<1, 5, 4>;               // 64 rows per workgroup (row groups of 64 above)
-
 //                 32-row blocks
 using CfgSV1 = SvCfg<1>;                       // 32 rows per workgroup
 using CfgSV2 = SvCfg<2>;                       // 64 rows per workgroup (row groups of 64 above)
@@ -54,7 +49,7 @@ using CfgG2 = GqaCfg<2>;                       // GQA path, two query tokens per
 
 // kS16: sparse (gathered-row) form of kR16; kG1 / kG2: GQA path; kRW4: 128 rows, one wave per
 // 32-row block
-enum CfgId { kR16 = 0, kW32, kW64, kS16, kG1, kG2, kSV1, kSV2, kRW4, kNumCfg };
+enum CfgId { kR16 = 0, kS16, kG1, kG2, kSV1, kSV2, kRW4, kNumCfg };
 
 struct LaunchGeom {
     CfgId cfg;
@@ -87,14 +82,12 @@ const void* split_fn(CfgId c)
 {
     switch (c) {
     case kR16: return reinterpret_cast<const void*>(&split_kernel<CfgR16>);
-    case kW32: return reinterpret_cast<const void*>(&split_wide_kernel<CfgW32>);
     case kS16: return reinterpret_cast<const void*>(&split_kernel<CfgR16, true>);
     case kG1: return reinterpret_cast<const void*>(&gqa_split_kernel<CfgG1>);
     case kG2: return reinterpret_cast<const void*>(&gqa_split_kernel<CfgG2>);
     case kSV1: return reinterpret_cast<const void*>(&split_sv_kernel<CfgSV1>);
     case kSV2: return reinterpret_cast<const void*>(&split_sv_kernel<CfgSV2>);
-    case kRW4: return split_rw_fn();
-    default: return reinterpret_cast<const void*>(&split_wide_kernel<CfgW64>);
+    default: return split_rw_fn();
     }
 }
 
@@ -165,11 +158,9 @@ int device_info(const DeviceInfo** out)
             d.status = MLA_ERR_NO_DEVICE;   // the code objects are built for gfx950 only
         } else {
             d.num_cu = prop.multiProcessorCount;
-            const int threads[kNumCfg] = {CfgR16::THREADS, CfgW32::THREADS, CfgW64::THREADS,
-                                          CfgR16::THREADS, kGqaThreads,     kGqaThreads,
+            const int threads[kNumCfg] = {CfgR16::THREADS, CfgR16::THREADS, kGqaThreads,     kGqaThreads,
                                           CfgSV1::THREADS, CfgSV2::THREADS, split_rw_threads()};
-            const int lds[kNumCfg] = {CfgR16::LDS_BYTES, CfgW32::LDS_BYTES, CfgW64::LDS_BYTES,
-                                      CfgR16::LDS_BYTES, CfgG1::LDS_BYTES,  CfgG2::LDS_BYTES,
+            const int lds[kNumCfg] = {CfgR16::LDS_BYTES, CfgR16::LDS_BYTES, CfgG1::LDS_BYTES,  CfgG2::LDS_BYTES,
                                       CfgSV1::LDS_BYTES, CfgSV2::LDS_BYTES, split_rw_lds_bytes()};
             for (int c = 0; c < kNumCfg; ++c) {
                 const void* fn = split_fn(static_cast<CfgId>(c));
@@ -309,11 +300,10 @@ int launch_split(const FwdArgs& a, const LaunchGeom& g, hipStream_t s)
     case kR16:
         hipLaunchKernelGGL(split_kernel<CfgR16>, dim3(a.capacity, g.row_groups), dim3(g.threads), g.lds_bytes, s, a);
         break;
-    case kW32: hipLaunchKernelGGL(split_wide_kernel<CfgW32>, dim3(blocks), dim3(g.threads), g.lds_bytes, s, a); break;
     case kSV1: hipLaunchKernelGGL(split_sv_kernel<CfgSV1>, dim3(blocks), dim3(g.threads), g.lds_bytes, s, a); break;
     case kSV2: hipLaunchKernelGGL(split_sv_kernel<CfgSV2>, dim3(blocks), dim3(g.threads), g.lds_bytes, s, a); break;
     case kRW4: launch_split_rw(a, blocks, s); break;
-    default: hipLaunchKernelGGL(split_wide_kernel<CfgW64>, dim3(blocks), dim3(g.threads), g.lds_bytes, s, a); break;
+    default: return MLA_ERR_HIP;   // not a split configuration of this entry point
     }
     return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }

@@ -676,467 +676,6 @@ __global__ void __launch_bounds__(C::THREADS) split_kernel(FwdArgs a)
 }
 
 // =============================================================================================
-// Split kernel, wide form (32 to 256 query rows per sequence; 128 is all heads on one GPU).
-//
-// A work item is taken by `row_groups` workgroups of 16 NRB query rows each (32 or 64; more
-// rows per sequence take more row groups).  Their ids are 8 apart
-// (id = 8 * row_group + item % 8 within a block of 8 * row_groups ids), so with round-robin
-// dispatch over the 8 XCDs they run together on one XCD and the second read of every KV tile
-// is served by that XCD's L2.
-//
-// Eight waves, two per SIMD, in two roles (the pages' split of the work between warp groups):
-//   score waves 0-3: wave w owns query rows 16w..16w+15 (Q^T in registers), computes
-//           S^T = K Q^T for them, keeps their online-softmax statistics and writes P^T (bf16)
-//           and the rescale factors to LDS;
-//   value waves 4-7: wave 4+w owns value dims 128w..128w+127 of all the group's rows and
-//           accumulates O^T += V^T P^T, reading each V^T operand once for all 16-row blocks.
-// With 32 rows, score waves 2-3 have no rows and only stage tiles.  With two waves per SIMD
-// one wave's MFMAs run while the other waits on LDS reads or tile data.
-// Both roles stream the KV tiles HBM -> VGPR -> LDS (each wave a fixed share of every tile).
-// Step t: score waves score tile t+1 and run the softmax of tile t; value waves accumulate
-// tile t-1; one barrier per step.  LDS holds four tile stages: t-1 (value), t (waiting for its
-// value step), t+1 (score), t+2 (landing).
-// =============================================================================================
-template <int NR_, int US_, int NRB_>
-struct WideCfg {
-    static constexpr int NW = 8;              // waves per workgroup: 4 score + 4 value
-    static constexpr int NRB = NRB_;          // 16-row blocks per workgroup (2 or 4)
-    static constexpr int RW = 16 * NRB;       // query rows per workgroup
-    static constexpr int TT = 32;             // tokens per tile
-    static constexpr int NS = 4;              // LDS stages
-    static constexpr int NR = NR_;            // tiles in flight in registers per wave
-    static constexpr int SEG = kDv / 4;       // value dims per value wave
-    static constexpr int DTW = SEG / 16;      // 16-dim output tiles per value wave
-    static constexpr int LDS_TILE = TT * kLdsRow;
-    static constexpr int UNITS = TT * kRowBytes / 1024;     // 1-KiB load units per tile (36)
-    static constexpr int US = US_;                          // units of an 8-row group a score wave moves
-    static constexpr int UV = 9 - US;                       // ... and its value-wave partner
-    static constexpr int P_ROW = TT * 2;                    // bytes of one P^T row (bf16)
-    static constexpr int P_BYTES = 64 * P_ROW;              // P^T of one tile (room for 64 rows)
-    static constexpr int OFF_P = NS * LDS_TILE;
-    static constexpr int OFF_ALPHA = OFF_P + 2 * P_BYTES;   // fp32 [2][64] rescale factors
-    static constexpr int OFF_FLAG = OFF_ALPHA + 2 * 64 * 4; // int [2][4] rescale flags
-    static constexpr int OFF_ML = OFF_FLAG + 2 * 4 * 4;     // fp32 [2][64] final m, l
-    static constexpr int LDS_BYTES = OFF_ML + 2 * 64 * 4;
-    static constexpr int THREADS = NW * 64;
-    static_assert(UNITS == 36, "four 8-row groups of nine 1-KiB units");
-    static_assert(NR == 1 || NR == 2, "one or two tiles in flight per wave");
-    static_assert(US >= 1 && US <= 9, "score waves move 1..9 units of their group");
-    static_assert(NRB == 2 || NRB == 4, "32 or 64 rows per workgroup");
-    static_assert(LDS_BYTES <= 160 * 1024, "LDS");
-};
-
-template <class C>
-__global__ void __launch_bounds__(C::THREADS) split_wide_kernel(FwdArgs a)
-{
-    extern __shared__ __attribute__((aligned(1024))) char smem[];
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int w4 = wave & 3;                 // row block (score) / dim segment (value) / 8-row group
-    const bool is_score = wave < 4;
-    const int lr = lane & 15;
-    const int lg = lane >> 4;
-
-    const int G = a.row_groups;
-    const int x = blockIdx.x;
-    const int item = (x / (8 * G)) * 8 + x % 8;
-    const int rg = (x / 8) % G;
-
-    const WsLayout lay = ws_layout(a.batch, a.rows, a.capacity);
-    // the arguments of the prologue's address computations come in with the first ones
-    asm volatile("" ::"s"(a.q), "s"(a.block_table), "s"(a.seqlens), "s"(a.bt_stride));
-    const PlanItem pi = read_plan_item(a, lay, item);
-    if (!pi.ok) return;   // a plan mismatch is reported by the combine kernel
-    const i32x4 it = pi.it;
-    const int b = it[0];
-    // the first block-table window and the lengths go out together (one round trip)
-    PageWindow pw;
-    pw.init(a.block_table + (size_t)b * a.bt_stride, a.bt_stride);
-    pw.prefetch(it[1], lane);
-    const int L = a.seqlens[b];
-    const int32_t plan_L = reinterpret_cast<const int32_t*>(a.ws + lay.seqlens)[b];
-    float* lse_part = reinterpret_cast<float*>(a.ws + lay.lse_part) + (size_t)item * a.rows;
-    float* o_part = reinterpret_cast<float*>(a.ws + lay.o_part) + (size_t)item * a.rows * kDv;
-
-    const int row_base = rg * C::RW;                  // first row of this group
-    const int srow = row_base + 16 * w4 + lr;         // score waves: this lane's row
-    const int qi = (row_base + 16 * w4) / a.heads;    // score waves: query token of the row block
-    // A sequence whose length disagrees with the plan or the table gets no tiles and a NaN LSE
-    // (no early exit: a branch here would make the loads above wait one after another).
-    const bool bad_seq = (L != plan_L) | (L < 0) | ((long long)L > (long long)kPage * a.bt_stride);
-    const int n_vis = a.causal ? min(max(L - a.s_q + 1 + qi, 0), L) : L;
-    const int tok_begin = it[1] * kPage;
-    const int tok_end = (int)min((long long)it[2] * kPage, (long long)L);   // it[2] * 64 may reach 2^31
-    const int n_tiles = bad_seq ? 0 : (tok_end - tok_begin + C::TT - 1) / C::TT;
-
-    // ---- tile staging, shared by both roles: the waves w and w + 4 move 8-row group w of every
-    // tile, the score wave units 0 .. US-1 and the value wave units US .. 8 of the group.  Lane l
-    // of unit u takes 16-B chunk 64 u + l of the group, which lands at LDS byte st9(u) of the
-    // group (rows padded to kLdsRow bytes).
-    const uint32_t lane16 = (uint32_t)lane * 16u;
-    auto st9 = [&](int v) __attribute__((always_inline)) {   // v is a compile-time constant
-        const int r0 = (64 * v) / kChunksPerRow;
-        const int bnd = kChunksPerRow * (r0 + 1) - 64 * v;
-        return v * 1024 + (kLdsRow - kRowBytes) * (r0 + (lane >= bnd ? 1 : 0)) + (int)lane16;
-    };
-    bool bad_page = bad_seq;
-    auto tile_rsrc = [&](int t) __attribute__((always_inline)) {
-        const int t0 = tok_begin + t * C::TT;
-        const int page = pw.page(t0 / kPage, lane);
-        int valid = min(C::TT, L - t0);
-        if (page < 0 || (long long)page >= a.num_pages) {
-            bad_page = true;
-            valid = 0;
-        }
-        const uint16_t* base = a.cache + ((long long)(valid ? page : 0) * kPage + (t0 % kPage)) * kDk;
-        return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, valid * kRowBytes, 0x00020000);
-    };
-    auto no_rsrc = [&]() __attribute__((always_inline)) {
-        return __builtin_amdgcn_make_buffer_rsrc((void*)a.cache, (short)0, 0, 0x00020000);
-    };
-    // U0: first unit of the group this wave moves; NU: how many
-    auto load_unit = [&](i32x4& dst, __amdgpu_buffer_rsrc_t rs, int u) __attribute__((always_inline)) {
-        dst = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)lane16, (9 * w4 + u) * 1024, kNonTemporal);
-    };
-    auto store_unit = [&](int t, const i32x4& src, int u) __attribute__((always_inline)) {
-        char* stg = smem + (t % C::NS) * C::LDS_TILE + w4 * (8 * kLdsRow);
-        *reinterpret_cast<i32x4*>(stg + st9(u)) = src;
-    };
-
-    const int kbase = lr * kLdsRow + 16 * lg;
-    const int vbase = (4 * lg + (lr >> 2)) * kLdsRow + 8 * (lr & 3) + 32 * (w4 * C::DTW);
-    // P^T: row r (64 B) keeps its 16-B chunk c at chunk c ^ ((r >> 2) & 3), so the 16 rows of a
-    // block read or written by one instruction spread over all LDS banks
-    const int pchunk = 16 * (lg ^ ((lr >> 2) & 3));
-    char* const pbuf0 = smem + C::OFF_P;
-    float* const alpha_s = reinterpret_cast<float*>(smem + C::OFF_ALPHA);
-    int* const flag_s = reinterpret_cast<int*>(smem + C::OFF_FLAG);
-    float* const ml_s = reinterpret_cast<float*>(smem + C::OFF_ML);
-    auto kread = [&](const char* p) __attribute__((always_inline)) { return *reinterpret_cast<const bf16x8*>(p); };
-    auto vread = [&](const char* p) __attribute__((always_inline)) {
-        return __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)lds_i16x4(p));
-    };
-    constexpr int NR = C::NR;
-
-    // One role's pipeline.  ROLE_STEP(t, buf, full, ...) runs step t; every wave runs the same
-    // steps and barriers.  Before step t: stages hold tiles t-1, t, t+1 (t+1 published), P^T(t-1)
-    // published, rbuf[t & (NR-1)] = tile t+2 (arrived or in flight), the other buffer tile t+3.
-    // Step t: store tile t+2, load tile t+2+NR, role work; barrier.
-    auto run_pipeline = [&](auto nu_tag, auto u0_tag, auto&& prologue_work, auto&& role_step,
-                            auto&& epilogue_work) __attribute__((always_inline)) {
-        constexpr int NU = decltype(nu_tag)::value;
-        constexpr int U0 = decltype(u0_tag)::value;
-        i32x4 rbuf[NR][NU > 0 ? NU : 1];
-        // kernel arguments the steps use are held in SGPRs from here on: a first use inside the
-        // loop would leave a scalar load pending there, and every LDS wait in the loop would
-        // then have to drain all LDS reads (lgkmcnt(0)) instead of the one it needs
-        asm volatile("" ::"s"(a.num_pages), "s"(a.cache), "s"(a.scale_log2));
-        // Loads are issued on every path (a tile past the end reads zeros through an empty
-        // resource and is never stored), so the number of loads in flight is the same on every
-        // path and each store waits only for its own unit.
-        auto load_all = [&](int t, auto buf) __attribute__((always_inline)) {
-            constexpr int B = decltype(buf)::value;
-            if constexpr (NU > 0) {
-                const __amdgpu_buffer_rsrc_t r = t < n_tiles ? tile_rsrc(t) : no_rsrc();
-#pragma unroll
-                for (int k = 0; k < NU; ++k) load_unit(rbuf[B][k], r, U0 + k);
-            }
-        };
-        auto store_all = [&](int t, auto buf) __attribute__((always_inline)) {
-            constexpr int B = decltype(buf)::value;
-#pragma unroll
-            for (int k = 0; k < NU; ++k) store_unit(t, rbuf[B][k], U0 + k);
-        };
-        // staging part of step t, spread over the role's k-steps: store unit k of tile t+2 in
-        // slot 2k, load it again (tile t+2+NR) in slot 2k+1
-        auto stage = [&](int t, auto buf, int slot, bool do_st, bool do_ld,
-                         __amdgpu_buffer_rsrc_t rs) __attribute__((always_inline)) {
-            constexpr int B = decltype(buf)::value;
-            const int k = slot >> 1;
-            if (NU > 0 && k < NU) {
-                if ((slot & 1) == 0) {
-                    if (do_st) store_unit(t + 2, rbuf[B][k], U0 + k);
-                } else {
-                    (void)do_ld;   // rs is empty when the tile is past the end
-                    load_unit(rbuf[B][k], rs, U0 + k);
-                }
-            }
-        };
-        if (n_tiles == 0) {   // uniform per workgroup: both roles skip the same barriers
-            epilogue_work();
-            return;
-        }
-        if constexpr (NR == 2) {
-            load_all(0, Idx<0>{});
-            load_all(1, Idx<1>{});
-            store_all(0, Idx<0>{});
-            load_all(2, Idx<0>{});
-            if (n_tiles > 1) store_all(1, Idx<1>{});
-            load_all(3, Idx<1>{});
-        } else {
-            // tiles 0 and 1 go out together (tile 1 waits in a second register set until tile 0
-            // is stored), so the prologue pays one memory round trip for them, not two
-            i32x4 rb1[NU > 0 ? NU : 1];
-            load_all(0, Idx<0>{});
-            if constexpr (NU > 0) {
-                const __amdgpu_buffer_rsrc_t r1 = 1 < n_tiles ? tile_rsrc(1) : no_rsrc();
-#pragma unroll
-                for (int k = 0; k < NU; ++k) load_unit(rb1[k], r1, U0 + k);
-            }
-            store_all(0, Idx<0>{});
-            load_all(2, Idx<0>{});
-            if (n_tiles > 1) {
-#pragma unroll
-                for (int k = 0; k < NU; ++k) store_unit(1, rb1[k], U0 + k);
-            }
-        }
-        __syncthreads();
-        prologue_work();
-        auto any_step = [&](int t, auto buf) __attribute__((always_inline)) {
-            const bool do_st = t + 2 < n_tiles, do_ld = NU > 0 && t + 2 + NR < n_tiles;
-            const __amdgpu_buffer_rsrc_t rs = do_ld ? tile_rsrc(t + 2 + NR) : no_rsrc();
-            role_step(t, Idx<0>{}, [&](int slot) __attribute__((always_inline)) {
-                stage(t, buf, slot, do_st, do_ld, rs);
-            });
-            __syncthreads();
-        };
-        auto full_step = [&](int t, auto buf) __attribute__((always_inline)) {
-            const __amdgpu_buffer_rsrc_t rs = NU > 0 ? tile_rsrc(t + 2 + NR) : no_rsrc();
-            role_step(t, Idx<1>{}, [&](int slot) __attribute__((always_inline)) {
-                stage(t, buf, slot, true, true, rs);
-            });
-            __syncthreads();
-        };
-        any_step(0, Idx<0>{});
-        int t = 1;
-        if constexpr (NR == 2 && NU > 0) {
-            for (; t + 3 + NR < n_tiles; t += 2) {   // steps t (odd) and t + 1 have every part
-                full_step(t, Idx<1>{});
-                full_step(t + 1, Idx<0>{});
-            }
-            for (; t < n_tiles; ++t) {
-                if (t & 1)
-                    any_step(t, Idx<1>{});
-                else
-                    any_step(t, Idx<0>{});
-            }
-        } else {
-            for (; t + 2 + NR < n_tiles; ++t) full_step(t, Idx<0>{});
-            for (; t < n_tiles; ++t) any_step(t, Idx<0>{});
-        }
-        epilogue_work();
-    };
-
-    constexpr float kLazyRescale = 8.f;
-    if (is_score && w4 >= C::NRB) {
-        // ================= staging only (score waves without rows) =================
-        run_pipeline(
-            Idx<C::US>{}, Idx<0>{}, [&]() __attribute__((always_inline)) {},
-            [&](int t, auto full, auto&& slot_fn) __attribute__((always_inline)) {
-#pragma unroll
-                for (int j = 0; j < 2 * C::US; ++j) slot_fn(j);
-            },
-            [&]() __attribute__((always_inline)) { __syncthreads(); });
-    } else if (is_score) {
-        // ================= score role =================
-        bf16x8 qop[kKSteps];
-        {
-            const uint16_t* qrow = a.q + ((size_t)(b * a.s_q + srow / a.heads) * a.heads + srow % a.heads) * kDk;
-#pragma unroll
-            for (int j = 0; j < kKSteps; ++j)
-                qop[j] = *reinterpret_cast<const bf16x8*>(qrow + 32 * j + 8 * lg);
-#pragma unroll
-            for (int j = 0; j < kKSteps; ++j) asm volatile("" ::"v"(qop[j]));
-        }
-        float m_run = -__builtin_inff();
-        float l_run = 0.f;   // lane-partial sum over this lane's tokens
-        f32x4 s[2];          // S^T of the tile awaiting its softmax: token 16 st + 4 lg + i of row srow
-        constexpr int KD = 3;   // K-operand look-ahead (k-steps of two MFMAs)
-        // S^T of tile ts; the staging slots and the softmax pieces of tile tsm run between the
-        // k-steps (softmax pieces read s, the new scores go to sn and replace s at the end)
-        auto score_step = [&](int ts, bool do_s, int tsm, bool do_sm, auto&& slot_fn) __attribute__((always_inline)) {
-            const char* sst = smem + (ts % C::NS) * C::LDS_TILE;
-            bf16x8 kop[KD + 1][2];
-            f32x4 sp[2][2];
-            if (do_s) {
-#pragma unroll
-                for (int st = 0; st < 2; ++st) {
-                    sp[st][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    sp[st][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int j = 0; j < KD; ++j) kop[j][st] = kread(sst + st * 16 * kLdsRow + kbase + 64 * j);
-                }
-            }
-            float tmax = 0.f;
-            bf16x8 pk;
-#pragma unroll
-            for (int j = 0; j < kKSteps; ++j) {
-                if (do_s) {
-                    if (j + KD < kKSteps) {
-#pragma unroll
-                        for (int st = 0; st < 2; ++st)
-                            kop[(j + KD) % (KD + 1)][st] = kread(sst + st * 16 * kLdsRow + kbase + 64 * (j + KD));
-                    }
-#pragma unroll
-                    for (int st = 0; st < 2; ++st)
-                        sp[st][j & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[j % (KD + 1)][st], qop[j],
-                                                                                sp[st][j & 1], 0, 0, 0);
-                }
-                if (do_sm) {
-                    const int par = tsm & 1;
-                    if (j == 1) {   // scale into the log2 domain, mask, lane max
-                        const int t0 = tok_begin + tsm * C::TT;
-#pragma unroll
-                        for (int st = 0; st < 2; ++st)
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) s[st][i] *= a.scale_log2;
-                        if (t0 + C::TT > n_vis) {   // only the tile holding the end of the visible keys
-#pragma unroll
-                            for (int st = 0; st < 2; ++st)
-#pragma unroll
-                                for (int i = 0; i < 4; ++i)
-                                    s[st][i] = (t0 + 16 * st + 4 * lg + i >= n_vis) ? -__builtin_inff() : s[st][i];
-                        }
-                        tmax = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-                    }
-                    if (j == 3) tmax = wave_max_groups(tmax);
-                    if (j == 5) {   // lazy max update; alpha and this block's flag go to LDS
-                        const bool resc = __builtin_amdgcn_ballot_w64(tmax > m_run + kLazyRescale) != 0;
-                        const float m_new = resc ? fmaxf(m_run, tmax) : m_run;
-                        const float alpha = (m_new == -__builtin_inff()) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-                        m_run = m_new;
-                        l_run *= alpha;
-                        alpha_s[par * 64 + 16 * w4 + lr] = alpha;   // the four lanes of a row agree
-                        flag_s[par * 4 + w4] = resc ? 1 : 0;
-                    }
-                    if (j == 7 || j == 9) {   // probabilities of one 16-token block
-                        const int h = (j - 7) / 2;
-                        const float m_use = (m_run == -__builtin_inff()) ? 0.f : m_run;
-                        float psum = 0.f;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const float pv = __builtin_amdgcn_exp2f(s[h][i] - m_use);
-                            psum += pv;
-                            pk[4 * h + i] = (__bf16)pv;
-                        }
-                        l_run += psum;
-                    }
-                    if (j == 11)   // P^T slot 8 lg + i holds token 4 lg + i (i < 4) or 16 + 4 lg + (i - 4)
-                        *reinterpret_cast<bf16x8*>(pbuf0 + par * C::P_BYTES + (16 * w4 + lr) * C::P_ROW + pchunk) = pk;
-                }
-                slot_fn(j);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            if (do_s) {
-#pragma unroll
-                for (int st = 0; st < 2; ++st) s[st] = sp[st][0] + sp[st][1];
-            }
-        };
-        run_pipeline(
-            Idx<C::US>{}, Idx<0>{},
-            [&]() __attribute__((always_inline)) {   // s = S^T(0)
-                if (n_tiles > 0) score_step(0, true, 0, false, [](int) {});
-            },
-            [&](int t, auto full, auto&& slot_fn) __attribute__((always_inline)) {
-                constexpr bool F = decltype(full)::value != 0;
-                score_step(t + 1, F || t + 1 < n_tiles, t, true, slot_fn);
-            },
-            [&]() __attribute__((always_inline)) {
-                l_run = wave_sum_groups(l_run);
-                if (lg == 0) {
-                    ml_s[16 * w4 + lr] = m_run;
-                    ml_s[64 + 16 * w4 + lr] = l_run;
-                    lse_part[srow] = bad_page ? __builtin_nanf("")
-                                              : (l_run > 0.f ? (m_run + __builtin_amdgcn_logf(l_run)) * kLn2
-                                                             : -__builtin_inff());
-                }
-                __syncthreads();
-            });
-    } else {
-        // ================= value role =================
-        // acc[dt][rb] holds O^T[SEG w4 + 16 dt + 4 lg + i][row_base + 16 rb + lr]
-        constexpr int NRB = C::NRB;
-        f32x4 acc[C::DTW][NRB];
-#pragma unroll
-        for (int dt = 0; dt < C::DTW; ++dt)
-#pragma unroll
-            for (int rb = 0; rb < NRB; ++rb) acc[dt][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        constexpr int VD = 2;   // V-operand look-ahead (16-dim tiles of four MFMAs)
-        auto value_step = [&](int tv, bool do_v, auto&& slot_fn) __attribute__((always_inline)) {
-            const char* vt0 = smem + (tv % C::NS) * C::LDS_TILE + vbase;
-            bf16x8 pop[NRB];
-            i16x4 vlo[VD + 1], vhi[VD + 1];
-            if (do_v) {
-                const int par = tv & 1;
-                // rows of a block that took a new max in tile tv: rescale their accumulators
-                const i32x4 flags = *reinterpret_cast<const i32x4*>(flag_s + par * 4);
-                // the operand reads go out behind the flags, so the flag check waits for one read
-                const char* pb = pbuf0 + par * C::P_BYTES;
-#pragma unroll
-                for (int rb = 0; rb < NRB; ++rb) pop[rb] = kread(pb + (16 * rb + lr) * C::P_ROW + pchunk);
-#pragma unroll
-                for (int d = 0; d < VD; ++d) {
-                    vlo[d] = vread(vt0 + 32 * d);
-                    vhi[d] = vread(vt0 + 16 * kLdsRow + 32 * d);
-                }
-#pragma unroll
-                for (int rb = 0; rb < NRB; ++rb) {
-                    if (__builtin_amdgcn_readfirstlane(flags[rb]) != 0) {
-                        const float al = alpha_s[par * 64 + 16 * rb + lr];
-#pragma unroll
-                        for (int dt = 0; dt < C::DTW; ++dt) {
-                            acc[dt][rb] *= al;
-                            __builtin_amdgcn_sched_barrier(0);
-                        }
-                    }
-                }
-            }
-#pragma unroll
-            for (int dt = 0; dt < C::DTW; ++dt) {
-                if (do_v) {
-                    if (dt + VD < C::DTW) {
-                        vlo[(dt + VD) % (VD + 1)] = vread(vt0 + 32 * (dt + VD));
-                        vhi[(dt + VD) % (VD + 1)] = vread(vt0 + 16 * kLdsRow + 32 * (dt + VD));
-                    }
-                    const bf16x8 vop = __builtin_shufflevector(__builtin_bit_cast(bf16x4, vlo[dt % (VD + 1)]),
-                                                               __builtin_bit_cast(bf16x4, vhi[dt % (VD + 1)]),
-                                                               0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-                    for (int rb = 0; rb < NRB; ++rb)
-                        acc[dt][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[rb], acc[dt][rb], 0, 0, 0);
-                }
-                slot_fn(dt);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            // the staging slots past the eight d-tiles
-#pragma unroll
-            for (int sl = C::DTW; sl < 2 * C::UV; ++sl) slot_fn(sl);
-        };
-        run_pipeline(
-            Idx<C::UV>{}, Idx<C::US>{}, [&]() __attribute__((always_inline)) {},
-            [&](int t, auto full, auto&& slot_fn) __attribute__((always_inline)) {
-                constexpr bool F = decltype(full)::value != 0;
-                value_step(t - 1, F || t >= 1, slot_fn);
-            },
-            [&]() __attribute__((always_inline)) {
-                if (n_tiles > 0) value_step(n_tiles - 1, true, [](int) {});   // value of the last tile
-                __syncthreads();
-#pragma unroll
-                for (int rb = 0; rb < NRB; ++rb) {
-                    const float l = ml_s[64 + 16 * rb + lr];
-                    const float inv = (l > 0.f) ? 1.f / l : 0.f;
-                    float* orow = o_part + (size_t)(row_base + 16 * rb + lr) * kDv + C::SEG * w4;
-#pragma unroll
-                    for (int dt = 0; dt < C::DTW; ++dt)
-                        store_partial(orow + 16 * dt + 4 * lg, acc[dt][rb] * inv);
-                }
-            });
-    }
-}
-
-// =============================================================================================
 // Combine: per (sequence, row) merge the items' normalised partials by their LSE,
 //   LSE = M + ln sum_s exp(LSE_s - M),  O = sum_s exp(LSE_s - LSE) O_s,
 // write O as bf16 (round to nearest even) and LSE as fp32.  NaN partials propagate; a row

@@ -12,7 +12,6 @@ using CfgRW4 = RwCfg<4>;   // 4 waves x 32 rows
 const void* split_rw_fn() { return reinterpret_cast<const void*>(&split_rw_kernel<CfgRW4>); }
 int split_rw_threads() { return CfgRW4::THREADS; }
 int split_rw_lds_bytes() { return CfgRW4::LDS_BYTES; }
-int split_rw_rows() { return CfgRW4::RW; }
 
 void launch_split_rw(const FwdArgs& a, int blocks, hipStream_t s)
 {
