@@ -83,8 +83,7 @@ def source_code_digest(texts) -> str:
 
 def kernel_source_digest() -> str:
     texts = []
-    for f in ("mla_decode_kernels.h", "mla_plan_kernel.h", "mla_sv_kernel.h", "mla_rw_kernel.h", "mla_decode.hip",
-              "mla_rw.hip"):
+    for f in ("mla_decode_kernels.h", "mla_plan_kernel.h", "mla_sv_kernel.h", "mla_decode.hip"):
         with open(os.path.join(ROOT, "mla_decode_attention_amd", "csrc", f)) as fh:
             texts.append(fh.read())
     return source_code_digest(texts)

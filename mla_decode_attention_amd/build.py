@@ -21,9 +21,8 @@ FLAGS = [
     "-Wall", "-Wno-unused-function",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
-# translation units of the library and whether each keeps the arch-VGPR accumulator option; the
-# 128-row kernel holds 256 accumulators per lane, which only fit in the AGPRs
-UNITS = [("mla_decode.hip", True), ("mla_rw.hip", False)]
+# translation units of the library and whether each keeps the arch-VGPR accumulator option
+UNITS = [("mla_decode.hip", True)]
 
 
 def _run(cmd: list[str], verbose: bool) -> None:

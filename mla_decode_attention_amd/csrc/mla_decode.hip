@@ -16,20 +16,6 @@
 #include "mla_plan_kernel.h"
 #include "mla_sv_kernel.h"
 
-// split kernel for more than 32 rows: 0 = paired score/value waves (64-row groups), 1 = one wave
-// per 32-row block (128-row groups)
-#ifndef MLA_WIDE_FORM
-#define MLA_WIDE_FORM 0
-#endif
-
-namespace mla {
-// the 128-row split kernel (mla_rw.hip, a translation unit of its own)
-const void* split_rw_fn();
-int split_rw_threads();
-int split_rw_lds_bytes();
-void launch_split_rw(const FwdArgs& a, int blocks, hipStream_t s);
-}  // namespace mla
-
 namespace {
 
 using namespace mla;
@@ -47,9 +33,8 @@ using CfgSV2 = SvCfg<2>;                       // 64 rows per workgroup (row gro
 using CfgG1 = GqaCfg<1>;                       // GQA path, one query token per step
 using CfgG2 = GqaCfg<2>;                       // GQA path, two query tokens per step
 
-// kS16: sparse (gathered-row) form of kR16; kG1 / kG2: GQA path; kRW4: 128 rows, one wave per
-// 32-row block
-enum CfgId { kR16 = 0, kS16, kG1, kG2, kSV1, kSV2, kRW4, kNumCfg };
+// kS16: sparse (gathered-row) form of kR16; kG1 / kG2: GQA path
+enum CfgId { kR16 = 0, kS16, kG1, kG2, kSV1, kSV2, kNumCfg };
 
 struct LaunchGeom {
     CfgId cfg;
@@ -70,11 +55,7 @@ bool geom_for(int s_q, int heads, LaunchGeom* g)
         *g = {kSV1, 1, CfgSV1::THREADS, CfgSV1::LDS_BYTES};
         return true;
     }
-#if MLA_WIDE_FORM == 0
     *g = {kSV2, (rows + 63) / 64, CfgSV2::THREADS, CfgSV2::LDS_BYTES};
-#else
-    *g = {kRW4, (rows + 127) / 128, split_rw_threads(), split_rw_lds_bytes()};
-#endif
     return true;
 }
 
@@ -86,8 +67,7 @@ const void* split_fn(CfgId c)
     case kG1: return reinterpret_cast<const void*>(&gqa_split_kernel<CfgG1>);
     case kG2: return reinterpret_cast<const void*>(&gqa_split_kernel<CfgG2>);
     case kSV1: return reinterpret_cast<const void*>(&split_sv_kernel<CfgSV1>);
-    case kSV2: return reinterpret_cast<const void*>(&split_sv_kernel<CfgSV2>);
-    default: return split_rw_fn();
+    default: return reinterpret_cast<const void*>(&split_sv_kernel<CfgSV2>);
     }
 }
 
@@ -158,10 +138,10 @@ int device_info(const DeviceInfo** out)
             d.status = MLA_ERR_NO_DEVICE;   // the code objects are built for gfx950 only
         } else {
             d.num_cu = prop.multiProcessorCount;
-            const int threads[kNumCfg] = {CfgR16::THREADS, CfgR16::THREADS, kGqaThreads,     kGqaThreads,
-                                          CfgSV1::THREADS, CfgSV2::THREADS, split_rw_threads()};
-            const int lds[kNumCfg] = {CfgR16::LDS_BYTES, CfgR16::LDS_BYTES, CfgG1::LDS_BYTES,  CfgG2::LDS_BYTES,
-                                      CfgSV1::LDS_BYTES, CfgSV2::LDS_BYTES, split_rw_lds_bytes()};
+            const int threads[kNumCfg] = {CfgR16::THREADS, CfgR16::THREADS, kGqaThreads,
+                                          kGqaThreads,     CfgSV1::THREADS, CfgSV2::THREADS};
+            const int lds[kNumCfg] = {CfgR16::LDS_BYTES, CfgR16::LDS_BYTES, CfgG1::LDS_BYTES,
+                                      CfgG2::LDS_BYTES,  CfgSV1::LDS_BYTES, CfgSV2::LDS_BYTES};
             for (int c = 0; c < kNumCfg; ++c) {
                 const void* fn = split_fn(static_cast<CfgId>(c));
                 int occ = 0;
@@ -302,7 +282,6 @@ int launch_split(const FwdArgs& a, const LaunchGeom& g, hipStream_t s)
         break;
     case kSV1: hipLaunchKernelGGL(split_sv_kernel<CfgSV1>, dim3(blocks), dim3(g.threads), g.lds_bytes, s, a); break;
     case kSV2: hipLaunchKernelGGL(split_sv_kernel<CfgSV2>, dim3(blocks), dim3(g.threads), g.lds_bytes, s, a); break;
-    case kRW4: launch_split_rw(a, blocks, s); break;
     default: return MLA_ERR_HIP;   // not a split configuration of this entry point
     }
     return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
