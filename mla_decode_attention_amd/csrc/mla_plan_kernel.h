@@ -87,7 +87,11 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(const int32_t* __res
     };
     if (tid == 0) scan_carry = 0;
     const long long total = block_sum(mine);
-    auto items_for = [&](long long c) { return block_sum(sum_pages([&](int pg) { return (pg + c - 1) / c; })); };
+    // (chunks are at most 2^25 pages: 32-bit divisions)
+    auto items_for = [&](long long c) {
+        const int c32 = (int)c;
+        return block_sum(sum_pages([&](int pg) { return (long long)((pg + c32 - 1) / c32); }));
+    };
     const long long slots = gx > 0 ? gx : 1;
     long long chunk;
     if (slots > batch) {
@@ -146,13 +150,18 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(const int32_t* __res
             // largest items.)  Deterministic: the split points depend only on the lengths.
             const bool weighted = total >= kWeightMinPages && (long long)pg >= 8LL * n;
             const int ev0 = (excl & 1) == 0 ? 1 : 0;   // item excl + s is even for s of this parity
+            // floor(a * b / c) in double precision: a * b < 2^53 is exact, the quotient is below
+            // 2^25, where doubles are 2^-28 apart, and a non-integer quotient is at least 1/c > 2^-27
+            // from the next integer, so the correctly rounded division floors to the exact result
+            // (an integer division of 64 bits would be a long software sequence per item)
+            auto muldiv = [](long long a, long long b, long long c) { return int(floor(double(a * b) / double(c))); };
             auto point = [&](int s) {
-                if (!weighted) return int((long long)s * pg / n);
+                if (!weighted) return muldiv(s, pg, n);   // s * pg <= pg^2 < 2^50
                 const long long e = (s + ev0) / 2;   // even items among the first s
                 const long long w = kEvenXcdWeight * e + kOddXcdWeight * (s - e);
                 const long long en = (n + ev0) / 2;
                 const long long wt = kEvenXcdWeight * en + kOddXcdWeight * (n - en);
-                return int((long long)pg * w / wt);
+                return muldiv(pg, w, wt);   // weighted: n <= pg / 8, so pg * w <= 2 pg^2 < 2^51
             };
             for (int s = 0; s < n; ++s) items[excl + s] = i32x4{b, point(s), point(s + 1), s};
         }

@@ -233,6 +233,19 @@ def test_plan_covers_every_page_once(dev, lens_kind):
                 assert (its[1:, 1] == its[:-1, 2]).all() and (its[:, 2] > its[:, 1]).all(), (b, L)
             sizes += (its[:, 2] - its[:, 1]).tolist()
             sz = its[:, 2] - its[:, 1]
+            # the split points, exactly: floor(s pg / n), or with 16 : 15 weights for even : odd items
+            n = len(its)
+            if n:
+                weighted = sum((x + 63) // 64 for x in lens) >= 8192 and pages >= 8 * n
+                ev0 = 1 if bs[b] % 2 == 0 else 0
+
+                def point(k):
+                    if not weighted:
+                        return k * pages // n
+                    e, en = (k + ev0) // 2, (n + ev0) // 2
+                    return pages * (16 * e + 15 * (k - e)) // (16 * en + 15 * (n - en))
+                assert its[:, 1].tolist() == [point(k) for k in range(n)], (b, L)
+                assert its[:, 2].tolist() == [point(k + 1) for k in range(n)], (b, L)
             if len(its) > 1 and pages >= 8 * len(its) and sum((x + 63) // 64 for x in lens) >= 8192:
                 # weighted (large plans): even-index items are not smaller
                 idx = np.arange(bs[b], bs[b + 1])
