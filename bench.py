@@ -181,10 +181,11 @@ def _cpu_model() -> str:
     return "unknown"
 
 
-def measure_workload(mla, name: str, dev, steps: int, warmup: int, parity_rows: int):
+def measure_workload(mla, name: str, dev, steps: int, warmup: int, parity_rows: int, flush_mib: int = 512):
     """One of the other configured workloads, timed like the headline: step (split + combine) and
-    split-kernel durations, algorithmic TB/s and MFMA utilisation, and raw parity of the first
-    parity_rows query rows against the fp64 oracle (reported, not asserted)."""
+    split-kernel durations, algorithmic TB/s and MFMA utilisation, the same per step after a cache
+    flush, and raw parity of the first parity_rows query rows against the fp64 oracle (reported,
+    not asserted)."""
     import numpy as np
     import torch
 
@@ -224,6 +225,29 @@ def measure_workload(mla, name: str, dev, steps: int, warmup: int, parity_rows: 
         combine_c()
     torch.cuda.synchronize()
     split_us = float(np.mean([ea[k].elapsed_time(eb[k]) for k in range(steps)])) * 1e3
+    # each step alone after 512 MiB (twice the last-level cache) went through the cache, so shapes
+    # whose keys fit that cache are timed reading them from HBM too: "read" leaves clean lines (as a
+    # model's other reads would), "write" dirty ones that must be written back as they are evicted
+    scratch = torch.empty(flush_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+    flushed = {}
+    for kind in ("read", "write"):
+        ef = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        for k in range(steps):
+            if kind == "write":
+                scratch.fill_(float(k))
+            else:
+                scratch.sum()
+            ef[k][0].record(stream)
+            split_c()
+            ef[k][1].record(stream)
+            combine_c()
+            ef[k][2].record(stream)
+        torch.cuda.synchronize()
+        f_step = float(np.median([ef[k][0].elapsed_time(ef[k][2]) for k in range(steps)])) * 1e3
+        f_split = float(np.median([ef[k][0].elapsed_time(ef[k][1]) for k in range(steps)])) * 1e3
+        flushed[kind] = (f_step, f_split)
+    del scratch
     nbytes = W.algorithmic_bytes(case.seqlens, b, s_q, h)
     flops = W.algorithmic_flops(case.seqlens, s_q, h, case.causal)
     kv_q = int(case.seqlens.astype(np.int64).sum()) * W.ROW_BYTES + b * s_q * h * 576 * 2
@@ -232,6 +256,10 @@ def measure_workload(mla, name: str, dev, steps: int, warmup: int, parity_rows: 
            "split_GB/s": round(kv_q / split_us / 1e3, 1),
            "mfma_util_step": round(flops / step_us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
            "mfma_util_split": round(flops / split_us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
+           "flushed": {kind: {"flush_mib": flush_mib, "median_us_per_step": round(fs, 2),
+                              "median_split_us": round(fp, 2), "TB/s": round(nbytes / fs / 1e6, 4),
+                              "mfma_util_step": round(flops / fs / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4)}
+                       for kind, (fs, fp) in flushed.items()},
            "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
            "config": {"batch": b, "s_q": s_q, "heads": h, "causal": bool(case.causal),
                       "context": [int(case.seqlens.min()), int(case.seqlens.max())]}}
@@ -391,6 +419,8 @@ def main() -> int:
     ap.add_argument("--flush-mib", type=int, default=0,
                     help="also time each step alone after overwriting this many MiB of scratch memory, so the "
                          "cache is read from HBM and not from the last-level cache (256 MB on MI355X)")
+    ap.add_argument("--flush-kind", choices=("write", "read"), default="write",
+                    help="how --flush-mib evicts the cache: overwrite the scratch (leaves dirty lines) or read it")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this size (for scaling PMC byte counters)")
     args = ap.parse_args()
@@ -504,7 +534,10 @@ def main() -> int:
         e = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
         torch.cuda.synchronize()
         for k in range(K):
-            scratch.fill_(float(k))
+            if args.flush_kind == "write":
+                scratch.fill_(float(k))
+            else:
+                scratch.sum()
             e[k][0].record(stream)
             split_c()
             e[k][1].record(stream)
@@ -514,7 +547,7 @@ def main() -> int:
         f_step = float(np.median([e[k][0].elapsed_time(e[k][2]) for k in range(K)]))
         f_split = float(np.median([e[k][0].elapsed_time(e[k][1]) for k in range(K)]))
         del scratch
-        flushed = {"flush_mib": args.flush_mib, "steps": K, "median_us_per_step": round(f_step * 1e3, 2),
+        flushed = {"flush_mib": args.flush_mib, "flush_kind": args.flush_kind, "steps": K, "median_us_per_step": round(f_step * 1e3, 2),
                    "median_split_us": round(f_split * 1e3, 2)}
         log(f"flushed: step median {f_step * 1e3:.1f} us, split median {f_split * 1e3:.1f} us")
 
