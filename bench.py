@@ -181,6 +181,38 @@ def _cpu_model() -> str:
     return "unknown"
 
 
+def flushed_medians(scratch, kind: str, steps: int, split_c, combine_c, stream):
+    """Median step (split + combine) and split-kernel durations in ms, each launch timed alone
+    right after the scratch went through the cache: kind "read" sums it (clean lines), "write"
+    fills it (dirty lines).  The step and the split are timed in separate loops, so that no event
+    sits between the split and the combine of a timed step."""
+    import numpy as np
+    import torch
+
+    def flush(k):
+        if kind == "write":
+            scratch.fill_(float(k))
+        else:
+            scratch.sum()
+
+    def timed(body):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        torch.cuda.synchronize()
+        for k in range(steps):
+            flush(k)
+            ev[k][0].record(stream)
+            body()
+            ev[k][1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ev]))
+
+    def step():
+        split_c()
+        combine_c()
+
+    return timed(step), timed(split_c)
+
+
 def measure_workload(mla, name: str, dev, steps: int, warmup: int, parity_rows: int, flush_mib: int = 512):
     """One of the other configured workloads, timed like the headline: step (split + combine) and
     split-kernel durations, algorithmic TB/s and MFMA utilisation, the same per step after a cache
@@ -231,22 +263,8 @@ def measure_workload(mla, name: str, dev, steps: int, warmup: int, parity_rows: 
     scratch = torch.empty(flush_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
     flushed = {}
     for kind in ("read", "write"):
-        ef = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-        torch.cuda.synchronize()
-        for k in range(steps):
-            if kind == "write":
-                scratch.fill_(float(k))
-            else:
-                scratch.sum()
-            ef[k][0].record(stream)
-            split_c()
-            ef[k][1].record(stream)
-            combine_c()
-            ef[k][2].record(stream)
-        torch.cuda.synchronize()
-        f_step = float(np.median([ef[k][0].elapsed_time(ef[k][2]) for k in range(steps)])) * 1e3
-        f_split = float(np.median([ef[k][0].elapsed_time(ef[k][1]) for k in range(steps)])) * 1e3
-        flushed[kind] = (f_step, f_split)
+        f_step, f_split = flushed_medians(scratch, kind, steps, split_c, combine_c, stream)
+        flushed[kind] = (f_step * 1e3, f_split * 1e3)
     del scratch
     nbytes = W.algorithmic_bytes(case.seqlens, b, s_q, h)
     flops = W.algorithmic_flops(case.seqlens, s_q, h, case.causal)
@@ -529,23 +547,9 @@ def main() -> int:
 
     flushed = None
     if args.flush_mib > 0:
-        # each step alone, after a fill kernel has overwritten flush_mib MiB (outside the timed region)
+        # each step alone, after flush_mib MiB went through the cache (outside the timed region)
         scratch = torch.empty(args.flush_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
-        e = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-        torch.cuda.synchronize()
-        for k in range(K):
-            if args.flush_kind == "write":
-                scratch.fill_(float(k))
-            else:
-                scratch.sum()
-            e[k][0].record(stream)
-            split_c()
-            e[k][1].record(stream)
-            combine_c()
-            e[k][2].record(stream)
-        torch.cuda.synchronize()
-        f_step = float(np.median([e[k][0].elapsed_time(e[k][2]) for k in range(K)]))
-        f_split = float(np.median([e[k][0].elapsed_time(e[k][1]) for k in range(K)]))
+        f_step, f_split = flushed_medians(scratch, args.flush_kind, K, split_c, combine_c, stream)
         del scratch
         flushed = {"flush_mib": args.flush_mib, "flush_kind": args.flush_kind, "steps": K, "median_us_per_step": round(f_step * 1e3, 2),
                    "median_split_us": round(f_split * 1e3, 2)}
