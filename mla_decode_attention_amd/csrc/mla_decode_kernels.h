@@ -451,8 +451,9 @@ __global__ void __launch_bounds__(C::THREADS) split_kernel(FwdArgs a)
         // scores S^T[token][row]: a dependent MFMA chain issues only every ~50 cycles, so each
         // 16-token block accumulates NCH independent partial sums over alternating k-steps
         // (NST * NCH = 4 chains in flight) that are added at the end; K operands are read KD
-        // k-steps ahead
-        constexpr int KD = C::NST == 1 ? 6 : 3;
+        // k-steps ahead (the gather form holds more addressing state: 4 keep it clear of spills,
+        // at the same speed)
+        constexpr int KD = C::NST == 1 ? (SPARSE ? 4 : 6) : 3;
         constexpr int NCH = C::NST >= 4 ? 1 : 4 / C::NST;
         f32x4 s[C::NST];
         f32x4 sp[C::NST][NCH];
