@@ -30,8 +30,8 @@ using CfgR16 = SplitCfg<4, 1, 1, 16, 1, 1>;    // 4 independent waves, one 18 Ki
 using CfgSV1 = SvCfg<1>;                       // 32 rows per workgroup
 using CfgSV2 = SvCfg<2>;                       // 64 rows per workgroup (row groups of 64 above)
 
-using CfgG1 = GqaCfg<1>;                       // GQA path, one query token per step
-using CfgG2 = GqaCfg<2>;                       // GQA path, two query tokens per step
+using CfgG1 = GqaCfg<1, 2>;                     // GQA path, one query token per step
+using CfgG2 = GqaCfg<2, 2>;                     // GQA path, two query tokens per step
 
 // kS16: sparse (gathered-row) form of kR16; kG1 / kG2: GQA path
 enum CfgId { kR16 = 0, kS16, kG1, kG2, kSV1, kSV2, kNumCfg };

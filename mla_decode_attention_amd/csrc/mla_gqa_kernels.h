@@ -40,13 +40,15 @@ constexpr int kGqaWaves = 4;
 constexpr int kGqaHeads = 16;
 constexpr int kGqaThreads = kGqaWaves * 64;
 
-template <int NRB_>   // 16-row blocks per wave = query tokens per sequence (s_q)
+template <int NRB_, int NR_>   // NRB: 16-row blocks per wave = query tokens per sequence (s_q)
 struct GqaCfg {
     static constexpr int NRB = NRB_;
+    static constexpr int NR = NR_;   // tiles in flight in registers per wave
     static constexpr int STAGE = kGqaTT * kGqaLdsRow;                                   // 10,752 B
     static constexpr int MERGE = kGqaWaves * NRB * 16 * (2 + kGqaDv) * 4;               // m, l, O per wave
     static constexpr int LDS_BYTES = kGqaWaves * STAGE > MERGE ? kGqaWaves * STAGE : MERGE;
     static_assert(NRB == 1 || NRB == 2, "one or two query tokens");
+    static_assert(NR == 1 || NR == 2, "one or two tiles in flight per wave");
 };
 
 template <class C>
@@ -102,8 +104,9 @@ __global__ void __launch_bounds__(kGqaThreads) gqa_split_kernel(FwdArgs a)
     const uint32_t lane16 = (uint32_t)lane * 16u;
     char* const stage = smem + wave * C::STAGE;
     bool bad_page = bad_seq;
-    i32x4 rbuf[kGqaUnits];
-    auto load_tile = [&](int itn) __attribute__((always_inline)) {
+    i32x4 rbuf[C::NR][kGqaUnits];
+    auto load_tile = [&](int itn, auto buf_idx) __attribute__((always_inline)) {
+        constexpr int B = decltype(buf_idx)::value;
         const int k = itn * kGqaWaves + wave;
         if (itn >= n_it || k >= n_tiles) return;
         const int t0 = tok_begin + k * kGqaTT;
@@ -118,16 +121,17 @@ __global__ void __launch_bounds__(kGqaThreads) gqa_split_kernel(FwdArgs a)
             __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, valid * kGqaRowBytes, 0x00020000);
 #pragma unroll
         for (int kk = 0; kk < kGqaUnits; ++kk)
-            rbuf[kk] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)lane16, kk * 1024, kNonTemporal);
+            rbuf[B][kk] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)lane16, kk * 1024, kNonTemporal);
     };
-    auto store_tile = [&](int itn) __attribute__((always_inline)) {
+    auto store_tile = [&](int itn, auto buf_idx) __attribute__((always_inline)) {
+        constexpr int B = decltype(buf_idx)::value;
         const int k = itn * kGqaWaves + wave;
         if (itn >= n_it || k >= n_tiles) return;
 #pragma unroll
         for (int kk = 0; kk < kGqaUnits; ++kk) {
             const int c = 64 * kk + lane;
             const int r = c / kGqaChunks;
-            *reinterpret_cast<i32x4*>(stage + r * kGqaLdsRow + 16 * (c - r * kGqaChunks)) = rbuf[kk];
+            *reinterpret_cast<i32x4*>(stage + r * kGqaLdsRow + 16 * (c - r * kGqaChunks)) = rbuf[B][kk];
         }
     };
 
@@ -204,21 +208,32 @@ __global__ void __launch_bounds__(kGqaThreads) gqa_split_kernel(FwdArgs a)
                                                                        acc[dt][rb], 0, 0, 0);
     };
 
-    // pipeline: tile itn+1 waits in registers while tile itn is computed from the stage
-    load_tile(0);
-    store_tile(0);
-    load_tile(1);
+    // pipeline: tiles itn+1 .. itn+NR wait in registers while tile itn is computed from the stage;
+    // then tile itn+1 is stored to the stage and its registers take tile itn+1+NR
+    load_tile(0, Idx<0>{});
+    if constexpr (C::NR == 2) load_tile(1, Idx<1>{});
+    store_tile(0, Idx<0>{});
+    load_tile(C::NR, Idx<0>{});
     // Consume Q here, so that no wait for it lands inside the tile loop (where it would also wait
     // for the tile loads in flight)
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
         for (int j = 0; j < kGqaKSteps; ++j) asm volatile("" ::"v"(qop[rb][j]));
-    for (int itn = 0; itn < n_it; ++itn) {
+    auto step = [&](int itn, auto next_buf) __attribute__((always_inline)) {
+        if (itn >= n_it) return;
         const int k = itn * kGqaWaves + wave;
         if (k < n_tiles) compute_tile(k);
-        store_tile(itn + 1);
-        load_tile(itn + 2);
+        store_tile(itn + 1, next_buf);
+        load_tile(itn + 1 + C::NR, next_buf);
+    };
+    if constexpr (C::NR == 2) {
+        for (int itn = 0; itn < n_it; itn += 2) {
+            step(itn, Idx<1>{});
+            step(itn + 1, Idx<0>{});
+        }
+    } else {
+        for (int itn = 0; itn < n_it; ++itn) step(itn, Idx<0>{});
     }
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) l_run[rb] = wave_sum_groups(l_run[rb]);
