@@ -53,6 +53,24 @@ def test_gqa_matches_oracle(dev, batch, s_q, lens, causal):
     parity(o, l, ro, rl, case.name)
 
 
+@pytest.mark.parametrize("s_q", [1, 2])
+def test_gqa_items_longer_than_a_block_table_window(dev, s_q):
+    """More sequences than resident split workgroups (512 with one query token, 256 with two), so
+    the plan makes every sequence one work item and the long ones span up to 141 pages: the kernel
+    refills its 64-entry block-table window inside an item, with two tiles in flight per wave.  The
+    pool holds four times the owned pages, the spare ones NaN, so a wrong page id shows."""
+    rng = np.random.default_rng(77 + s_q)
+    lens = [int(x) for x in rng.integers(0, 100, 520)]
+    lens[5], lens[100], lens[300], lens[511] = 9000, 5000, 64 * 70 + 3, 64 * 65
+    need = sum((L + 63) // 64 for L in lens)
+    case = _gqa_case(f"gqa_long_items_sq{s_q}", len(lens), s_q, lens, seed=78, causal=s_q == 2,
+                     pool_pages=4 * need, table_slack=5)
+    log(f"gqa {case.name}: {len(lens)} sequences, longest {max(lens)} tokens, pool {4 * need} pages")
+    o, l = _run(case, dev)
+    ro, rl = G.gqa_decode(case.q, case.cache, case.block_table, case.seqlens, case.softmax_scale, case.causal)
+    parity(o, l, ro, rl, case.name)
+
+
 def test_gqa_bad_page_gives_nan(dev):
     case = _gqa_case("gqa_bad", 3, 2, [300, 200, 500], seed=72, causal=True)
     bt = case.block_table.copy()
