@@ -241,19 +241,6 @@ struct PageWindow {
     }
 };
 
-// LDS-destination buffer load of 16 B per lane: lane l's bytes land at LDS byte lds + 16 l (M0
-// holds the wave's LDS address).  Written as inline asm, with no register output, so that the
-// compiler, which cannot tell the tile being loaded from the tiles being read, does not make the
-// wave's LDS reads wait for it; the issuing wave waits for its own loads (vm_wait_all) before the
-// barrier that publishes the tile.
-__device__ inline void lds_load_16(__amdgpu_buffer_rsrc_t r, uint32_t lds, int voffset)
-{
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voffset), "s"(r)
-                 : "memory", "m0");
-}
-
-__device__ inline void vm_wait_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0) only
-
 // Partial outputs are written once and read once by the combine kernel on whichever XCD it runs:
 // streaming (non-temporal) stores send them on to memory during the kernel instead of leaving
 // them dirty in this XCD's L2 for the write-back at the kernel's end.

@@ -18,18 +18,22 @@
 //   value waves 4-7  wave 4 + v owns value dims 128 v .. 128 v + 127 of all the rows:
 //                    O^T += V^T P^T with v_mfma_f32_32x32x16_bf16 (V^T read straight from the
 //                    row-major tile with transposing LDS reads), and moves a quarter of every
-//                    tile HBM -> LDS with LDS-destination buffer loads.
+//                    tile HBM -> VGPR -> LDS (16-B non-temporal buffer loads, two tiles in flight
+//                    in registers per wave).
 // Per 32-token tile every SIMD runs 36 score MFMAs (16x16x32) and 16 value MFMAs (32x32x16):
 // 576 + 512 cycles of its matrix pipe.  On gfx950 a wave's own vector instructions and waits
 // stall its next MFMA while the other wave's do not (measured), so every SIMD keeps two
 // MFMA-issuing waves, each covering the other's stalls.
 //
 // Pipeline (one barrier per step): step t scores tile t + 1 and runs the softmax of tile t
-// (score waves), accumulates tile t - 1 (value waves) and loads tile t + 2; tile k is loaded
-// at step k - 2, scored at k - 1, weighted at k, accumulated at k + 1, so LDS holds four stages.
+// (score waves), accumulates tile t - 1 (value waves), stores tile t + 2 from registers to LDS
+// and loads tile t + 4 into the registers it leaves; tile k is loaded at step k - 4, stored at
+// k - 2, scored at k - 1, weighted at k, accumulated at k + 1, so LDS holds four stages and
+// every load has two steps to arrive.  (Loading straight into LDS would leave each load one
+// step: the four stages are all in use.)
 //
 // LDS tile layout: row r at r * 1184 B (74 16-B chunks: the 16-row K-operand read hits 32
-// distinct bank groups); a tile is 37 KiB exactly, and the two pad chunks of a row load zeros.
+// distinct bank groups); a row's two pad chunks are never written or read.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -62,9 +66,9 @@ struct SvCfg {
     static constexpr int NS = 4;                               // LDS tile stages
     static constexpr int LCH = kChunksPerRow + 2;              // 74 16-B chunks per LDS tile row
     static constexpr int LROW = LCH * 16;                      // 1184 B
-    static constexpr int LDS_TILE = TT * LROW;                 // 37888 B: 37 units of 1 KiB
-    static constexpr int UNITS = LDS_TILE / 1024;              // 37
-    static constexpr int UV = (UNITS + 3) / 4;                 // units per value wave (10; waves 5-7 move 9)
+    static constexpr int LDS_TILE = TT * LROW;                 // 37888 B
+    static constexpr int UNITS = TT * kRowBytes / 1024;        // 36 one-KiB load units per tile
+    static constexpr int UV = UNITS / 4;                       // units per value wave
     static constexpr int KSTEPS = kDk / 32;                    // 18 score k-steps of 32
     static constexpr int OFF_P = NS * LDS_TILE;                // P^T [2 parity][rb][ks][64 lanes][16 B]
     static constexpr int P_BYTES = 2 * 2 * 1024;
@@ -74,7 +78,7 @@ struct SvCfg {
     static constexpr int OFF_ML = OFF_FLAG + 2 * 2 * 4;        // fp32 [3][64]: m, l of half 0, l of half 1
     static constexpr int OFF_BAD = OFF_ML + 3 * 64 * 4;        // int [8]: per-wave bad-page flags
     static constexpr int LDS_BYTES = OFF_BAD + 8 * 4;
-    static_assert(LDS_TILE % 1024 == 0, "whole 1-KiB units");
+    static_assert(UV * 4 == UNITS, "four value waves, whole units each");
     static_assert(NRB == 1 || NRB == 2, "32 or 64 rows per workgroup");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
     static_assert(RW * kOutRow <= NS * LDS_TILE, "partial rows fit the tile stages");
@@ -120,6 +124,20 @@ __global__ void __launch_bounds__(C::THREADS) split_sv_kernel(FwdArgs a)
     auto stage = [&](int t) __attribute__((always_inline)) { return smem + (t % C::NS) * C::LDS_TILE; };
     constexpr float kLazyRescale = 8.f;
     bool bad_page = false;
+    asm volatile("" ::"s"(a.num_pages), "s"(a.cache));
+    // buffer resource of tile t (rows past L_b and past the last tile read as zeros)
+    auto tile_rsrc = [&](PageWindow& pw, int t) __attribute__((always_inline)) {
+        if (t >= n_tiles) return __builtin_amdgcn_make_buffer_rsrc((void*)a.cache, (short)0, 0, 0x00020000);
+        const int t0 = tok_begin + t * C::TT;
+        const int page = pw.page(t0 / kPage, lane);
+        int valid = min(C::TT, L - t0);
+        if (page < 0 || (long long)page >= a.num_pages) {
+            bad_page = true;
+            valid = 0;
+        }
+        const uint16_t* base = a.cache + ((long long)(valid ? page : 0) * kPage + (t0 % kPage)) * kDk;
+        return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, valid * kRowBytes, 0x00020000);
+    };
 
     if (wave < 4) {
         // ================= score waves =================
@@ -293,37 +311,40 @@ __global__ void __launch_bounds__(C::THREADS) split_sv_kernel(FwdArgs a)
         const int v = wave - 4;   // value dims 128 v .. 128 v + 127
         constexpr int NRB = C::NRB;
         const int l32 = lane & 31, g = lane >> 5;
-        // ---- tile loads: units u = v + 4 k; lane l of unit u fills LDS chunk c = 64 u + l = 74 r + k
-        // of the tile with cache chunk 72 r + k, or zeros for a row's two pad chunks (an offset past
-        // the resource's end reads zeros)
+        // ---- tile staging HBM -> VGPR -> LDS, two tiles in flight per wave: units u = v + 4 k of a
+        // tile's 36 one-KiB units; lane l of unit u holds cache chunk c = 64 u + l (row c / 72),
+        // which goes to LDS byte 16 (c + 2 (c / 72)) (rows padded to 74 chunks)
         PageWindow pw;
         pw.init(a.block_table + (size_t)b * a.bt_stride, a.bt_stride);
         pw.prefetch(it[1], lane);
-        asm volatile("" ::"s"(a.num_pages), "s"(a.cache));
-        int voff[C::UV];
+        int soff[C::UV];
 #pragma unroll
         for (int k = 0; k < C::UV; ++k) {
             const int c = 64 * (v + 4 * k) + lane;
-            const int r = c / C::LCH, ch = c % C::LCH;
-            voff[k] = ch < kChunksPerRow ? 16 * (kChunksPerRow * r + ch) : (1 << 30);
+            soff[k] = 16 * (c + 2 * (c / kChunksPerRow));
         }
-        const int my_units = (C::UNITS - v + 3) / 4;   // 10 for wave 4, 9 for the others
-        auto load_tile = [&](int t) __attribute__((always_inline)) {
-            if (t >= n_tiles) return;
-            const int t0 = tok_begin + t * C::TT;
-            const int page = pw.page(t0 / kPage, lane);
-            int valid = min(C::TT, L - t0);
-            if (page < 0 || (long long)page >= a.num_pages) {
-                bad_page = true;
-                valid = 0;
-            }
-            const uint16_t* base = a.cache + ((long long)(valid ? page : 0) * kPage + (t0 % kPage)) * kDk;
-            const __amdgpu_buffer_rsrc_t r =
-                __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, valid * kRowBytes, 0x00020000);
-            const uint32_t st = (uint32_t)(uintptr_t)(MLA_LDS char*)stage(t);
+        i32x4 sbuf[2][C::UV];
+        // loads are issued on every path (past the last tile through an empty resource, which
+        // reads zeros without a memory access), so every store waits only for its own units
+        auto load = [&](int t, auto bi) __attribute__((always_inline)) {
+            constexpr int B = decltype(bi)::value;
+            const __amdgpu_buffer_rsrc_t r = tile_rsrc(pw, t);
 #pragma unroll
             for (int k = 0; k < C::UV; ++k)
-                if (k < my_units) lds_load_16(r, st + 1024 * (v + 4 * k), voff[k]);
+                sbuf[B][k] = __builtin_amdgcn_raw_buffer_load_b128(r, 16 * lane, 1024 * (v + 4 * k), kNonTemporal);
+        };
+        auto store = [&](int t, auto bi) __attribute__((always_inline)) {
+            constexpr int B = decltype(bi)::value;
+            char* st = stage(t);
+#pragma unroll
+            for (int k = 0; k < C::UV; ++k) *reinterpret_cast<i32x4*>(st + soff[k]) = sbuf[B][k];
+        };
+        // the loads of one step (unit k of tile t + 4, into the registers tile t + 2 has just left)
+        // go out one per MFMA group of the value product: issued in one burst, they stall the wave
+        // on a full memory queue while its MFMAs wait behind them
+        auto slot = [&](int k, auto bi, __amdgpu_buffer_rsrc_t r) __attribute__((always_inline)) {
+            constexpr int B = decltype(bi)::value;
+            sbuf[B][k] = __builtin_amdgcn_raw_buffer_load_b128(r, 16 * lane, 1024 * (v + 4 * k), kNonTemporal);
         };
 
         // acc[d][rb]: O^T[128 v + 32 d + 8 (r / 4) + 4 g + r % 4][row 32 rb + l32], register r
@@ -338,7 +359,7 @@ __global__ void __launch_bounds__(C::THREADS) split_sv_kernel(FwdArgs a)
         auto vread = [&](const char* p) __attribute__((always_inline)) {
             return __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)lds_i16x4(p));
         };
-        auto value_step = [&](int tv) __attribute__((always_inline)) {
+        auto value_step = [&](int tv, auto&& slot_fn) __attribute__((always_inline)) {
             const int par = tv & 1;
             const int2 flags = *reinterpret_cast<const int2*>(flag_s + par * 2);
             const char* pb = pbuf + par * C::P_BYTES + 16 * lane;
@@ -381,25 +402,44 @@ __global__ void __launch_bounds__(C::THREADS) split_sv_kernel(FwdArgs a)
 #pragma unroll
                 for (int rb = 0; rb < NRB; ++rb)
                     acc[d][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[rb][ks], acc[d][rb], 0, 0, 0);
+                slot_fn(i);
                 __builtin_amdgcn_sched_barrier(0);
             }
+            slot_fn(8);
+        };
+        // step t: store tile t + 2 from sbuf[t & 1] and load tile t + 4 into it, then accumulate
+        // tile t - 1
+        auto step = [&](int t, auto bi) __attribute__((always_inline)) {
+            const __amdgpu_buffer_rsrc_t r = tile_rsrc(pw, t + 4);
+            auto sl = [&](int k) __attribute__((always_inline)) { slot(k, bi, r); };
+            if (t + 2 < n_tiles) store(t + 2, bi);
+            if (t >= 1) {
+                value_step(t - 1, sl);
+            } else {
+#pragma unroll
+                for (int k = 0; k < C::UV; ++k) sl(k);
+            }
+            __syncthreads();
         };
         if (n_tiles > 0) {
-            load_tile(0);
-            load_tile(1);
-            vm_wait_all();
+            load(0, Idx<0>{});
+            load(1, Idx<1>{});
+            store(0, Idx<0>{});
+            load(2, Idx<0>{});
+            if (n_tiles > 1) store(1, Idx<1>{});
+            load(3, Idx<1>{});
             __syncthreads();   // tiles 0 and 1 are in LDS
             __syncthreads();   // the score waves' tile-0 maxima
-            for (int t = 0; t < n_tiles; ++t) {   // step t
-                load_tile(t + 2);
-                if (t >= 1) value_step(t - 1);
-                vm_wait_all();
-                __syncthreads();
+            int t = 0;
+            for (; t + 1 < n_tiles; t += 2) {
+                step(t, Idx<0>{});
+                step(t + 1, Idx<1>{});
             }
+            if (t < n_tiles) step(t, Idx<0>{});
         }
         bad_s[wave] = (bad_page || bad_seq) ? 1 : 0;
         __syncthreads();   // E1: (m, l) of every row are in LDS; P^T of the last tile too
-        if (n_tiles > 0) value_step(n_tiles - 1);
+        if (n_tiles > 0) value_step(n_tiles - 1, [](int) {});
         __syncthreads();   // E2: every value wave is done with the tile stages
         // normalised partial rows into LDS, [row][dim] with rows padded to 2064 B (rows 16 B apart in
         // the bank space), so that they leave as whole contiguous rows below
