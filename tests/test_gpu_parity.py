@@ -114,33 +114,41 @@ def _workspace_for(mla, case, sl, dev):
     return (ws,)
 
 
-def test_bad_page_and_mismatched_plan_give_nan_not_fault(dev):
+@pytest.mark.parametrize("heads,s_q", [(16, 1), (16, 2), (128, 1), (48, 2)])
+def test_bad_page_and_mismatched_plan_give_nan_not_fault(dev, heads, s_q):
+    """A page id outside the pool poisons only its sequence (NaN O and LSE), in the 16-row kernel
+    and in the paired kernel's 32-row and 64-row forms; a plan made for other lengths or another
+    head count poisons the whole batch.  No case reads outside the cache."""
     import torch
 
     import mla_decode_attention_amd as mla
-    case = make_case("badpage", batch=3, s_q=1, heads=16, seqlen=[200, 300, 100], seed=36)
+    causal = s_q == 2
+    case = make_case(f"badpage_h{heads}_sq{s_q}", batch=3, s_q=s_q, heads=heads, seqlen=[200, 300, 100], seed=36,
+                     causal=causal)
     q, cache, bt, sl = to_device(case, dev)
     bt_bad = bt.clone()
     bt_bad[1, 2] = case.num_pages + 7          # out of the pool
-    out, lse = mla.decode(q, cache, bt_bad, sl, case.softmax_scale, False)
+    out, lse = mla.decode(q, cache, bt_bad, sl, case.softmax_scale, causal)
     torch.cuda.synchronize()
     o = out.float().cpu().numpy()
     l = lse.cpu().numpy()
     assert np.isnan(o[1]).all() and np.isnan(l[1]).all()
-    ro, rl = oracle.mla_decode(case.q, case.cache, case.block_table, case.seqlens, case.softmax_scale, False)
-    parity(o[[0, 2]], l[[0, 2]], ro[[0, 2]], rl[[0, 2]], "sequences beside a bad page")
+    ro, rl = oracle.mla_decode(case.q, case.cache, case.block_table, case.seqlens, case.softmax_scale, causal)
+    parity(o[[0, 2]], l[[0, 2]], ro[[0, 2]], rl[[0, 2]], f"sequences beside a bad page (h{heads} s_q{s_q})")
     # plan made for other seqlens
-    ws = torch.empty(mla.workspace_size(3, 1, 16), dtype=torch.uint8, device=dev)
-    mla.plan(sl + 1, 1, 16, ws)
+    ws = torch.empty(mla.workspace_size(3, s_q, heads), dtype=torch.uint8, device=dev)
+    mla.plan(sl + 1, s_q, heads, ws)
     out2 = torch.empty_like(out)
     lse2 = torch.empty_like(lse)
-    mla.fwd(q, cache, bt, sl, case.softmax_scale, False, ws, out2, lse2)
+    mla.fwd(q, cache, bt, sl, case.softmax_scale, causal, ws, out2, lse2)
     torch.cuda.synchronize()
     assert torch.isnan(lse2).all()
     # plan made for another head count: the whole batch is NaN
-    ws3 = torch.empty(mla.workspace_size(3, 1, 32), dtype=torch.uint8, device=dev)
-    mla.plan(sl, 1, 32, ws3)
-    mla.fwd(q, cache, bt, sl, case.softmax_scale, False, ws3, out2, lse2)
+    other = 32 if heads != 32 else 64
+    nbytes = max(mla.workspace_size(3, s_q, other), mla.workspace_size(3, s_q, heads))
+    ws3 = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    mla.plan(sl, s_q, other, ws3)
+    mla.fwd(q, cache, bt, sl, case.softmax_scale, causal, ws3, out2, lse2)
     torch.cuda.synchronize()
     assert torch.isnan(lse2).all() and torch.isnan(out2.float()).all()
 
