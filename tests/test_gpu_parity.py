@@ -74,8 +74,12 @@ def test_seeded_shape_sweep(dev, heads, s_q, causal, lens, scale, seed):
     full_parity(case, dev, f"{case.name} scale={scale:.4g}")
 
 
-def test_empty_and_single_key_sequences(dev):
-    case = make_case("empty_mix", batch=5, s_q=2, heads=16, seqlen=[0, 1, 2, 0, 70], seed=32, causal=True)
+@pytest.mark.parametrize("heads", [16, 64, 128])
+def test_empty_and_single_key_sequences(dev, heads):
+    """Empty sequences (no work item), one and two keys (a causal first token that sees nothing or
+    one key), in the 32-row, 128-row and 256-row forms."""
+    case = make_case(f"empty_mix_h{heads}", batch=5, s_q=2, heads=heads, seqlen=[0, 1, 2, 0, 70], seed=32,
+                     causal=True)
     full_parity(case, dev)
 
 
