@@ -97,16 +97,20 @@ def test_outlier_rows_softmax_max_tracking(dev):
     full_parity(case, dev)
 
 
-def test_deterministic_for_a_plan(dev):
+@pytest.mark.parametrize("heads,s_q", [(16, 1), (16, 2), (128, 1)])
+def test_deterministic_for_a_plan(dev, heads, s_q):
+    """The same inputs and plan give bit-identical O and LSE on a rerun, in every kernel form."""
     import torch
 
     import mla_decode_attention_amd as mla
-    case = make_case("det", batch=3, s_q=1, heads=16, seqlen=[5000, 130, 2048], seed=35)
+    causal = s_q == 2
+    case = make_case(f"det_h{heads}_sq{s_q}", batch=3, s_q=s_q, heads=heads, seqlen=[5000, 130, 2048], seed=35,
+                     causal=causal)
     q, cache, bt, sl = to_device(case, dev)
-    out1, lse1 = mla.decode(q, cache, bt, sl, case.softmax_scale, False)
+    out1, lse1 = mla.decode(q, cache, bt, sl, case.softmax_scale, causal)
     out2, lse2 = out1.clone(), lse1.clone()
     out1.zero_()
-    mla.fwd(q, cache, bt, sl, case.softmax_scale, False, *_workspace_for(mla, case, sl, dev), out1, lse1)
+    mla.fwd(q, cache, bt, sl, case.softmax_scale, causal, *_workspace_for(mla, case, sl, dev), out1, lse1)
     torch.cuda.synchronize()
     assert torch.equal(out1.view(torch.int16), out2.view(torch.int16)) and torch.equal(lse1, lse2)
 
